@@ -1,0 +1,175 @@
+/*
+ * fsattn.h -- C ABI of the Fused-Softmax quantized-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("Fused-Softmax shifts an AI attention bottleneck onto faster
+ * GPU hardware", cybernoise.de article on arXiv 2611.09225, paragraphs 5-6;
+ * "Fused softmax makes quantized attention faster on AMD GPUs", chiosa.app,
+ * section "What the evidence shows" / "Move work, keep correction"):
+ * attention O = softmax(Q K^T) V with Q, K, V MX-quantized; the row-max
+ * reference is provisionally frozen and its subtraction, together with the
+ * affine part of Schraudolph's exponential, is folded into the Q K^T matrix
+ * product; P is produced by a two-stage conversion (a BF16 bit pattern, then
+ * MX); the normalisation sum is the product P.1 fed the same quantized P as
+ * P V; a rollback gate raises the reference and rescales O and l when a
+ * tile's scores exceed the reference by more than tau.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller (allocate
+ *    them with the size helpers below).  The library allocates nothing,
+ *    keeps no mutable global state and is safe to call from several host
+ *    threads.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously on it; the call returns once enqueued.
+ *  - Arguments are validated on the host before anything is launched.  On
+ *    any error nothing is launched and a negative fsattn_status is returned.
+ *    Empty problems (a zero-sized dimension) return FSATTN_OK without a
+ *    launch.  A launch failure is reported as FSATTN_E_HIP.
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef FSATTN_H
+#define FSATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSATTN_ABI_VERSION 1
+
+typedef enum {
+  FSATTN_OK = 0,
+  FSATTN_E_INVALID_ARG = -1, /* null pointer, bad size, bad enum value */
+  FSATTN_E_UNSUPPORTED = -2, /* valid request this build does not implement */
+  FSATTN_E_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned */
+  FSATTN_E_HIP = -4          /* the HIP runtime reported an error */
+} fsattn_status;
+
+/* MX element formats (OCP Microscaling v1.0).  The values equal the gfx950
+ * matrix-core format selectors. */
+typedef enum {
+  FSATTN_E4M3 = 0, /* FP8,  max 448   */
+  FSATTN_E5M2 = 1, /* FP8,  max 57344 */
+  FSATTN_E2M3 = 2, /* FP6,  max 7.5   */
+  FSATTN_E3M2 = 3, /* FP6,  max 28    */
+  FSATTN_E2M1 = 4  /* FP4,  max 6     */
+} fsattn_elem;
+
+/* E8M0 block-scale rule.  FITMAX: the smallest power of two X with
+ * max|x|/X <= the format's largest value (no element saturates).
+ * OCP_FLOOR: X = 2^(floor(log2 max|x|) - emax), elements above the largest
+ * value saturate. */
+typedef enum { FSATTN_SCALE_FITMAX = 0, FSATTN_SCALE_OCP_FLOOR = 1 } fsattn_scale_rule;
+
+int fsattn_abi_version(void);
+const char* fsattn_status_str(int status);
+
+/*
+ * ---- MX byte layout -----------------------------------------------------
+ * A block is 32 elements sharing one E8M0 scale byte (value 2^(s-127)).
+ * Codes of a block are packed into 32*bits/8 bytes: 8-bit codes one per
+ * byte; 6-bit codes as a little-endian bit stream (element j occupies bits
+ * [6j, 6j+6) of the 24 bytes); 4-bit codes two per byte, element 2i in the
+ * low nibble of byte i.
+ *
+ * block_axis 0 (Q, K: blocks along the feature dimension):
+ *   input  [n_mat][rows][cols] bf16 (row stride ld elements), cols % 32 == 0
+ *   codes  [n_mat][rows][cols/32][block bytes]
+ *   scales [n_mat][rows][cols/32]
+ * block_axis 1 (V: blocks along keys), stored transposed, key-contiguous:
+ *   input  [n_mat][rows][cols] bf16, rows = keys, cols = features
+ *   codes  [n_mat][cols][rows32/32][block bytes], rows32 = rows rounded up to 32
+ *   scales [n_mat][cols][rows32/32]; keys >= rows are zero padding.
+ */
+int64_t fsattn_mx_codes_bytes(int elem, int64_t n_mat, int64_t rows, int64_t cols, int block_axis);
+int64_t fsattn_mx_scales_bytes(int64_t n_mat, int64_t rows, int64_t cols, int block_axis);
+
+/*
+ * fsattn_quantize_mx -- MX-quantize a bf16 tensor (Q, K or V).
+ * Quantized operands of the method ("Fused-Softmax shifts an AI attention
+ * bottleneck ...", paragraphs 7-8: MXFP8 / MXFP6 / MXFP4 configurations).
+ *
+ *  src        device bf16, layout above; ld >= cols.
+ *  prescale   every value becomes fl32(prescale * x) before quantization.
+ *             For Q pass 128 * log2(e) * softmax_scale rounded to fp32: this
+ *             is the multiplicative part of the fold (the Schraudolph slope
+ *             and the softmax scale).  K and V: 1.0f.
+ *  elem, rule element format and E8M0 rule.
+ *  codes_out, scales_out  device buffers of fsattn_mx_*_bytes() bytes.
+ *  Per block: amax -> E8M0 -> each element x/X rounded to nearest-even in
+ *  the element format (sign of zero kept).  Results are bit-exact with the
+ *  definition above.  NaN/Inf inputs are outside the contract.
+ *  Errors: FSATTN_E_INVALID_ARG (null, negative sizes, cols % 32 != 0 on
+ *  axis 0, ld < cols, bad enum), FSATTN_E_ALIGNMENT (src, codes_out or
+ *  scales_out not 16-byte aligned), FSATTN_E_HIP.
+ */
+int fsattn_quantize_mx(const void* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld, int block_axis,
+                       float prescale, int elem, int rule, void* codes_out, uint8_t* scales_out, void* stream);
+
+/* An MX operand as produced by fsattn_quantize_mx. */
+typedef struct {
+  int elem;              /* fsattn_elem */
+  float prescale;        /* the prescale it was quantized with */
+  const void* codes;     /* device */
+  const uint8_t* scales; /* device */
+} fsattn_mx_tensor;
+
+typedef struct {
+  int B, H;              /* batch, heads */
+  int Sq, Skv;           /* query and key counts (>= 1 for Skv, any length: tails are masked) */
+  int D;                 /* head dimension: 64 or 128 */
+  float softmax_scale;   /* sigma; must equal q->prescale / (128 log2 e) to within 2 ulp */
+  int p_elem;            /* element format of P: E4M3 or E2M3 */
+  float tau;             /* rollback threshold in log2 units of P, >= 0 (default 8) */
+  float schraudolph_c;   /* shift c in BF16-pattern units (default 0) */
+  int kv_tile;           /* keys per gate tile: 64 or 128 */
+  int32_t* rollback_counts; /* optional device [B][H][Sq]: fires per query row; NULL = not written */
+  uint8_t* p_dump_codes;    /* optional device [(p_row1-p_row0)][Skv32], one code per key, for rows
+                               [p_row0, p_row1) of head (p_b, p_h); NULL = no dump */
+  uint8_t* p_dump_scales;   /* optional device [(p_row1-p_row0)][Skv32/32] E8M0 of P */
+  int p_b, p_h, p_row0, p_row1;
+} fsattn_params;
+
+/*
+ * fsattn_forward -- Fused-Softmax attention forward on MX operands.
+ *
+ * q: [B][H][Sq][D] codes on block_axis 0 quantized with prescale
+ *    128*log2(e)*softmax_scale; k: [B][H][Skv][D] block_axis 0; v: block_axis
+ *    1 with rows = Skv ([B][H][D][Skv32]).  Q and K share one element format
+ *    (E4M3, E2M3 or E2M1); V is E4M3, E2M3 or E2M1.
+ * out: device bf16 [B][H][Sq][D].
+ *
+ * Per query row i and kv tile j (kv_tile keys, ascending):
+ *   t = fl32(C_i + sum_d Qhat_id Khat_kd)   (tile 0: C_i = 0, then
+ *       C_i = floor(T0 - max t), t += C_i; T0 = fl32(128*127 - c))
+ *   rollback: if max_k t > T_gate = fl32(128*(127+tau) - c) (tiles j >= 1),
+ *       delta = ceil(max t - T0); t -= delta; C_i -= delta;
+ *       O_i, l_i *= 2^(-delta/128); count_i += 1
+ *   stage 1: b = floor(t) as a BF16 bit pattern (0 if t < 128, at most 0x7F7F)
+ *   stage 2: P = MX(bf16(b)) per 32 consecutive keys (fit-max E8M0)
+ *   O_i += P V, l_i += P 1 (same P); finally O_i / l_i rounded to bf16.
+ * Errors: FSATTN_E_INVALID_ARG (null, sizes, D not 64/128, kv_tile not
+ * 64/128, tau < 0, prescale/softmax_scale mismatch, bad dump window),
+ * FSATTN_E_UNSUPPORTED (format combination), FSATTN_E_ALIGNMENT, FSATTN_E_HIP.
+ */
+int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsattn_mx_tensor* k,
+                   const fsattn_mx_tensor* v, void* out, void* stream);
+
+/*
+ * fsattn_forward_bf16_baseline -- conventional attention forward in BF16
+ * (the baseline the pages compare against, paragraph 8): tiled online
+ * softmax with a running max and rescaling ("Conventional implementations
+ * repeatedly update a reference maximum and rescale", paragraph 5), BF16
+ * matrix products with fp32 accumulation, exp2 in fp32.
+ * q [B][H][Sq][D], k, v [B][H][Skv][D], out [B][H][Sq][D]; all bf16, device,
+ * contiguous.  D = 64 or 128.
+ * Errors: FSATTN_E_INVALID_ARG, FSATTN_E_ALIGNMENT, FSATTN_E_HIP.
+ */
+int fsattn_forward_bf16_baseline(const void* q, const void* k, const void* v, int B, int H, int Sq, int Skv,
+                                 int D, float softmax_scale, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FSATTN_H */

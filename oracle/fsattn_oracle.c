@@ -236,6 +236,63 @@ static double bf16_to_double(uint16_t h) {
   return (double)f;
 }
 
+typedef struct {
+  const uint16_t* src;
+  int64_t n_mat, rows, cols, ld;
+  int block_axis, elem, rule;
+  float prescale;
+  uint8_t *codes, *scales;
+  int64_t nunits; /* axis 0: n_mat*rows rows; axis 1: n_mat*cols columns */
+  int64_t next;
+  pthread_mutex_t mu;
+} quant_job_t;
+
+/* quantize every block of one unit (a row on axis 0, a column on axis 1) */
+static void quant_unit(const quant_job_t* J, int64_t u) {
+  int bb = fso_block_bytes(J->elem);
+  double x[32];
+  uint8_t c[32];
+  if (J->block_axis == 0) {
+    int64_t m = u / J->rows, r = u % J->rows, nb = J->cols / 32;
+    const uint16_t* s = J->src + m * J->rows * J->ld + r * J->ld;
+    for (int64_t g = 0; g < nb; ++g) {
+      for (int j = 0; j < 32; ++j) {
+        double v = bf16_to_double(s[g * 32 + j]);
+        x[j] = (J->prescale == 1.0f) ? v : (double)(float)((double)J->prescale * v);
+      }
+      fso_mxq_block(J->elem, J->rule, x, 32, c, J->scales + u * nb + g);
+      pack_block(J->elem, c, J->codes + (u * nb + g) * bb);
+    }
+  } else {
+    int64_t m = u / J->cols, col = u % J->cols;
+    int64_t nb = (J->rows + 31) / 32;
+    const uint16_t* s = J->src + m * J->rows * J->ld;
+    for (int64_t g = 0; g < nb; ++g) {
+      for (int j = 0; j < 32; ++j) {
+        int64_t r = g * 32 + j;
+        double v = (r < J->rows) ? bf16_to_double(s[r * J->ld + col]) : 0.0;
+        x[j] = (J->prescale == 1.0f) ? v : (double)(float)((double)J->prescale * v);
+      }
+      fso_mxq_block(J->elem, J->rule, x, 32, c, J->scales + u * nb + g);
+      pack_block(J->elem, c, J->codes + (u * nb + g) * bb);
+    }
+  }
+}
+
+static void* quant_worker(void* arg) {
+  quant_job_t* J = (quant_job_t*)arg;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int64_t u0 = J->next;
+    J->next += 64;
+    pthread_mutex_unlock(&J->mu);
+    if (u0 >= J->nunits) break;
+    int64_t u1 = u0 + 64 < J->nunits ? u0 + 64 : J->nunits;
+    for (int64_t u = u0; u < u1; ++u) quant_unit(J, u);
+  }
+  return NULL;
+}
+
 int fso_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
                     int block_axis, float prescale, int elem, int rule,
                     uint8_t* codes, uint8_t* scales) {
@@ -243,39 +300,20 @@ int fso_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t co
       ld < cols)
     return FSO_EINVAL;
   if (block_axis == 0 && cols % 32) return FSO_EINVAL;
-  int bb = fso_block_bytes(elem);
-  int64_t rows32 = (rows + 31) / 32 * 32;
-  double x[32];
-  uint8_t c[32];
-  for (int64_t m = 0; m < n_mat; ++m) {
-    const uint16_t* s = src + m * rows * ld;
-    if (block_axis == 0) {
-      int64_t nb = cols / 32;
-      for (int64_t r = 0; r < rows; ++r)
-        for (int64_t g = 0; g < nb; ++g) {
-          for (int j = 0; j < 32; ++j) {
-            double v = bf16_to_double(s[r * ld + g * 32 + j]);
-            x[j] = (prescale == 1.0f) ? v : (double)(float)((double)prescale * v);
-          }
-          uint8_t* sc = scales + (m * rows + r) * nb + g;
-          fso_mxq_block(elem, rule, x, 32, c, sc);
-          pack_block(elem, c, codes + ((m * rows + r) * nb + g) * bb);
-        }
-    } else {
-      int64_t nb = rows32 / 32;
-      for (int64_t col = 0; col < cols; ++col)
-        for (int64_t g = 0; g < nb; ++g) {
-          for (int j = 0; j < 32; ++j) {
-            int64_t r = g * 32 + j;
-            double v = (r < rows) ? bf16_to_double(s[r * ld + col]) : 0.0;
-            x[j] = (prescale == 1.0f) ? v : (double)(float)((double)prescale * v);
-          }
-          uint8_t* sc = scales + (m * cols + col) * nb + g;
-          fso_mxq_block(elem, rule, x, 32, c, sc);
-          pack_block(elem, c, codes + ((m * cols + col) * nb + g) * bb);
-        }
-    }
-  }
+  quant_job_t J;
+  J.src = src; J.n_mat = n_mat; J.rows = rows; J.cols = cols; J.ld = ld;
+  J.block_axis = block_axis; J.elem = elem; J.rule = rule; J.prescale = prescale;
+  J.codes = codes; J.scales = scales;
+  J.nunits = block_axis == 0 ? n_mat * rows : n_mat * cols;
+  J.next = 0;
+  pthread_mutex_init(&J.mu, NULL);
+  int nt = fso_default_threads();
+  if (nt > 64) nt = 64;
+  if ((int64_t)nt > J.nunits / 64 + 1) nt = (int)(J.nunits / 64 + 1);
+  pthread_t th[64];
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, quant_worker, &J);
+  for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+  pthread_mutex_destroy(&J.mu);
   return FSO_OK;
 }
 

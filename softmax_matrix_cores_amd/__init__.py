@@ -1,0 +1,186 @@
+"""softmax_matrix_cores_amd -- Fused-Softmax quantized attention on AMD MI355X.
+
+Thin ctypes binding over the C ABI in ``include/fsattn.h`` (``libfsattn.so``,
+built in-tree by ``softmax_matrix_cores_amd.build``).  This module only
+marshals arguments: every step of the attention path runs in the HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: if the library is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsattn.so")
+
+E4M3, E5M2, E2M3, E3M2, E2M1 = 0, 1, 2, 3, 4
+ELEMS = {"e4m3": E4M3, "e5m2": E5M2, "e2m3": E2M3, "e3m2": E3M2, "e2m1": E2M1}
+ELEM_BITS = {E4M3: 8, E5M2: 8, E2M3: 6, E3M2: 6, E2M1: 4}
+SCALE_FITMAX, SCALE_OCP_FLOOR = 0, 1
+
+# every symbol include/fsattn.h declares
+ABI_SYMBOLS = (
+    "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
+    "fsattn_quantize_mx", "fsattn_forward", "fsattn_forward_bf16_baseline",
+)
+
+
+class FsattnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().fsattn_status_str(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+
+
+class _MxTensor(ctypes.Structure):
+    _fields_ = [("elem", ctypes.c_int), ("prescale", ctypes.c_float), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("Sq", ctypes.c_int), ("Skv", ctypes.c_int), ("D", ctypes.c_int),
+        ("softmax_scale", ctypes.c_float), ("p_elem", ctypes.c_int), ("tau", ctypes.c_float),
+        ("schraudolph_c", ctypes.c_float), ("kv_tile", ctypes.c_int),
+        ("rollback_counts", ctypes.c_void_p), ("p_dump_codes", ctypes.c_void_p), ("p_dump_scales", ctypes.c_void_p),
+        ("p_b", ctypes.c_int), ("p_h", ctypes.c_int), ("p_row0", ctypes.c_int), ("p_row1", ctypes.c_int),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfsattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m softmax_matrix_cores_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        V, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.fsattn_abi_version.restype = I
+        L.fsattn_status_str.restype = ctypes.c_char_p
+        L.fsattn_status_str.argtypes = [I]
+        L.fsattn_mx_codes_bytes.restype = I64
+        L.fsattn_mx_codes_bytes.argtypes = [I, I64, I64, I64, I]
+        L.fsattn_mx_scales_bytes.restype = I64
+        L.fsattn_mx_scales_bytes.argtypes = [I64, I64, I64, I]
+        L.fsattn_quantize_mx.restype = I
+        L.fsattn_quantize_mx.argtypes = [V, I64, I64, I64, I64, I, ctypes.c_float, I, I, V, V, V]
+        L.fsattn_forward.restype = I
+        L.fsattn_forward.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
+                                     ctypes.POINTER(_MxTensor), V, V]
+        L.fsattn_forward_bf16_baseline.restype = I
+        L.fsattn_forward_bf16_baseline.argtypes = [V, V, V, I, I, I, I, I, ctypes.c_float, V, V]
+        _lib = L
+    return _lib
+
+
+def _elem(e) -> int:
+    return ELEMS[e] if isinstance(e, str) else int(e)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise FsattnError(fn, status)
+
+
+def fold_prescale(softmax_scale: float) -> float:
+    """fl32(128 * log2(e) * softmax_scale): the multiplicative part of the fold."""
+    return float(torch.tensor(128.0 * math.log2(math.e) * softmax_scale, dtype=torch.float64).float())
+
+
+@dataclass
+class MXTensor:
+    codes: torch.Tensor   # uint8, packed codes
+    scales: torch.Tensor  # uint8, E8M0
+    elem: int
+    prescale: float
+
+    def _c(self) -> _MxTensor:
+        return _MxTensor(self.elem, self.prescale, self.codes.data_ptr(), self.scales.data_ptr())
+
+
+def mx_sizes(elem, n_mat: int, rows: int, cols: int, block_axis: int) -> tuple[int, int]:
+    e = _elem(elem)
+    cb = lib().fsattn_mx_codes_bytes(e, n_mat, rows, cols, block_axis)
+    sb = lib().fsattn_mx_scales_bytes(n_mat, rows, cols, block_axis)
+    if cb < 0 or sb < 0:
+        raise ValueError("invalid MX tensor shape")
+    return cb, sb
+
+
+def quantize_mx(x: torch.Tensor, block_axis: int, elem, prescale: float = 1.0, rule: int = SCALE_FITMAX,
+                stream=None, out: MXTensor | None = None) -> MXTensor:
+    """MX-quantize a contiguous bf16 CUDA tensor viewed as [n_mat, rows, cols] (last two dims)."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda:
+        raise TypeError("quantize_mx expects a bf16 CUDA tensor")
+    x = x.contiguous()
+    rows, cols = x.shape[-2], x.shape[-1]
+    n_mat = x.numel() // max(1, rows * cols) if rows * cols else 0
+    e = _elem(elem)
+    cb, sb = mx_sizes(e, n_mat, rows, cols, block_axis)
+    if out is None:
+        codes = torch.empty(cb, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(sb, dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out.codes, out.scales
+    st = lib().fsattn_quantize_mx(x.data_ptr(), n_mat, rows, cols, cols, block_axis, ctypes.c_float(prescale), e,
+                                  rule, codes.data_ptr(), scales.data_ptr(), _stream(stream))
+    _check("fsattn_quantize_mx", st)
+    return MXTensor(codes, scales, e, float(torch.tensor(prescale, dtype=torch.float32)))
+
+
+def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qk_elem, v_elem, softmax_scale: float,
+                 stream=None) -> tuple[MXTensor, MXTensor, MXTensor]:
+    """Quantize [B,H,S,D] bf16 Q (with the folded prescale), K and V (blocks along keys)."""
+    Q = quantize_mx(q, 0, qk_elem, prescale=fold_prescale(softmax_scale), stream=stream)
+    K = quantize_mx(k, 0, qk_elem, stream=stream)
+    V = quantize_mx(v, 1, v_elem, stream=stream)
+    return Q, K, V
+
+
+def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv: int, D: int, softmax_scale: float,
+            p_elem, tau: float = 8.0, c: float = 0.0, kv_tile: int = 64, counts: torch.Tensor | None = None,
+            out: torch.Tensor | None = None, p_dump: tuple | None = None, stream=None) -> torch.Tensor:
+    """Fused-Softmax attention forward.  Returns bf16 [B,H,Sq,D].
+    counts: optional int32 [B,H,Sq] written with rollback counts.
+    p_dump: optional (b, h, row0, row1, codes uint8 [rows, Skv32], scales uint8 [rows, Skv32/32])."""
+    dev = Q.codes.device
+    if out is None:
+        out = torch.empty(B, H, Sq, D, dtype=torch.bfloat16, device=dev)
+    p = _Params(B, H, Sq, Skv, D, softmax_scale, _elem(p_elem), tau, c, kv_tile,
+                counts.data_ptr() if counts is not None else None, None, None, 0, 0, 0, 0)
+    if p_dump is not None:
+        b, h, r0, r1, pc, ps = p_dump
+        p.p_dump_codes, p.p_dump_scales = pc.data_ptr(), ps.data_ptr()
+        p.p_b, p.p_h, p.p_row0, p.p_row1 = b, h, r0, r1
+    q, k, v = Q._c(), K._c(), V._c()
+    st = lib().fsattn_forward(ctypes.byref(p), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out.data_ptr(),
+                              _stream(stream))
+    _check("fsattn_forward", st)
+    return out
+
+
+def forward_bf16_baseline(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float,
+                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Conventional BF16 attention forward (online softmax).  q [B,H,Sq,D], k/v [B,H,Skv,D]."""
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib().fsattn_forward_bf16_baseline(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Sq, Skv, D,
+                                            ctypes.c_float(softmax_scale), out.data_ptr(), _stream(stream))
+    _check("fsattn_forward_bf16_baseline", st)
+    return out

@@ -1,0 +1,127 @@
+"""Helpers shared by the GPU parity tests: run the HIP path and the oracle on the
+same seeded bf16 inputs and compare by the acceptance criteria
+(global relative Frobenius error <= 1e-2, P-code mismatch fraction <= 1e-3,
+rollback counts equal per row, quantizer bytes identical)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import softmax_matrix_cores_amd as fs
+from softmax_matrix_cores_amd import workloads as W
+
+REL_FROB_TOL = 1e-2
+P_MISMATCH_TOL = 1e-3
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bits(x: torch.Tensor) -> np.ndarray:
+    return x.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def oracle_quant(O, q, k, v, w: W.Workload):
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    qk, ve = O.ELEM_NAMES[w.qk_elem], O.ELEM_NAMES[w.v_elem]
+    alpha = O.softmax_scale_prescale(w.sigma)
+    Qo = O.quantize_mx(bits(q).reshape(B * H, Sq, D), 0, qk, prescale=alpha)
+    Ko = O.quantize_mx(bits(k).reshape(B * H, Skv, D), 0, qk)
+    Vo = O.quantize_mx(bits(v).reshape(B * H, Skv, D), 1, ve)
+    return Qo, Ko, Vo
+
+
+def gpu_quant(q, k, v, w: W.Workload):
+    dev = torch.device("cuda:0")
+    return fs.quantize_qkv(q.to(dev), k.to(dev), v.to(dev), w.qk_elem, w.v_elem, w.sigma)
+
+
+def same_bytes(gpu: fs.MXTensor, ora) -> tuple[bool, bool]:
+    gc = gpu.codes.cpu().numpy().ravel()
+    gs = gpu.scales.cpu().numpy().ravel()
+    return np.array_equal(gc, ora[0].ravel()), np.array_equal(gs, ora[1].ravel())
+
+
+def oracle_params(O, w: W.Workload, tau=None, kv_tile=None):
+    return O.make_params(w.B, w.H, w.Sq, w.Skv, w.D, O.ELEM_NAMES[w.qk_elem], O.ELEM_NAMES[w.v_elem],
+                         O.ELEM_NAMES[w.p_elem], tau=w.tau if tau is None else tau,
+                         kv_tile=w.kv_tile if kv_tile is None else kv_tile)
+
+
+def rel_frob(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def p_mismatch(gc, gs, oc, os_) -> float:
+    """Fraction of P elements whose code or block scale differs."""
+    gs_e = np.repeat(gs, 32, axis=1)[:, : gc.shape[1]]
+    os_e = np.repeat(os_, 32, axis=1)[:, : oc.shape[1]]
+    bad = (gc != oc) | (gs_e != os_e)
+    return float(bad.mean())
+
+
+def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=None, kv_tile=None,
+             check_quant=True):
+    """Full comparison on workload w.  rows: oracle row sample (None = all rows).
+    Returns a dict of metrics; asserts nothing."""
+    log(f"[case] {w.name} B={w.B} H={w.H} Sq={w.Sq} Skv={w.Skv} D={w.D} {w.qk_elem}/{w.v_elem}/{w.p_elem} "
+        f"tau={w.tau if tau is None else tau} kv_tile={w.kv_tile if kv_tile is None else kv_tile}")
+    q, k, v = W.make_inputs(w)
+    tau_ = w.tau if tau is None else tau
+    kvt = w.kv_tile if kv_tile is None else kv_tile
+    res = {}
+    # GPU path
+    Qg, Kg, Vg = gpu_quant(q, k, v, w)
+    counts = torch.zeros(w.B, w.H, w.Sq, dtype=torch.int32, device="cuda:0")
+    s32 = (w.Skv + 31) // 32 * 32
+    pd = None
+    if dump_rows is not None:
+        r0, r1 = dump_rows
+        pc = torch.zeros(r1 - r0, s32, dtype=torch.uint8, device="cuda:0")
+        ps = torch.zeros(r1 - r0, s32 // 32, dtype=torch.uint8, device="cuda:0")
+        pd = (dump_head[0], dump_head[1], r0, r1, pc, ps)
+    out = fs.forward(Qg, Kg, Vg, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=tau_, kv_tile=kvt,
+                     counts=counts, p_dump=pd)
+    torch.cuda.synchronize()
+    log(f"[case] {w.name}: GPU done")
+    # oracle
+    Qo, Ko, Vo = oracle_quant(O, q, k, v, w)
+    if check_quant:
+        res["quant_q"] = same_bytes(Qg, Qo)
+        res["quant_k"] = same_bytes(Kg, Ko)
+        res["quant_v"] = same_bytes(Vg, Vo)
+    p = oracle_params(O, w, tau=tau_, kv_tile=kvt)
+    row_ids = None if rows is None else np.asarray(rows, dtype=np.int64)
+    r = O.forward(p, Qo, Ko, Vo, rows=row_ids)
+    gout = out.float().cpu().numpy().reshape(-1, w.D)
+    gcnt = counts.cpu().numpy().ravel()
+    if row_ids is not None:
+        gout = gout[row_ids]
+        gcnt = gcnt[row_ids]
+    res["rel_frob"] = rel_frob(gout.astype(np.float64), r["O"])
+    res["count_mismatch_rows"] = int((gcnt != r["counts"]).sum())
+    res["total_counts"] = int(r["counts"].sum())
+    res["finite"] = bool(np.isfinite(gout).all())
+    if dump_rows is not None:
+        b, h, r0, r1 = pd[:4]
+        drows = (b * w.H + h) * w.Sq + np.arange(r0, r1)
+        rd = O.forward(p, Qo, Ko, Vo, rows=drows, want_p=True)
+        res["p_mismatch"] = p_mismatch(pd[4].cpu().numpy(), pd[5].cpu().numpy(), rd["p_codes"], rd["p_scales"])
+    log(f"[case] {w.name}: {res}")
+    return res
+
+
+def assert_ok(res: dict):
+    for key in ("quant_q", "quant_k", "quant_v"):
+        if key in res:
+            assert res[key] == (True, True), (key, res)
+    assert res["finite"], res
+    assert res["rel_frob"] <= REL_FROB_TOL, res
+    assert res["count_mismatch_rows"] == 0, res
+    if "p_mismatch" in res:
+        assert res["p_mismatch"] <= P_MISMATCH_TOL, res

@@ -1,0 +1,101 @@
+"""The C-ABI library: it loads, exports every symbol include/fsattn.h declares,
+its size helpers follow the documented byte layout, and argument validation
+rejects bad calls before anything is launched (no GPU needed for these)."""
+import ctypes
+import re
+import os
+
+import pytest
+
+import softmax_matrix_cores_amd as fs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "fsattn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsattn_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = fs.lib()
+    decl = header_functions()
+    assert set(decl) == set(fs.ABI_SYMBOLS), decl
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings():
+    L = fs.lib()
+    assert L.fsattn_abi_version() == 1
+    for s in (0, -1, -2, -3, -4):
+        assert L.fsattn_status_str(s)
+    assert L.fsattn_status_str(-99) == b"unknown status"
+
+
+@pytest.mark.parametrize("elem,bits", [(0, 8), (1, 8), (2, 6), (3, 6), (4, 4)])
+def test_size_helpers(elem, bits):
+    # axis 0: [n][rows][cols/32] blocks
+    assert fs.mx_sizes(elem, 2, 5, 128, 0) == (2 * 5 * 4 * bits * 4, 2 * 5 * 4)
+    # axis 1: [n][cols][ceil(rows/32)] blocks
+    assert fs.mx_sizes(elem, 3, 75600, 128, 1) == (3 * 128 * 2363 * bits * 4, 3 * 128 * 2363)
+    with pytest.raises(ValueError):
+        fs.mx_sizes(elem, 1, 4, 100, 0)  # cols % 32
+
+
+def _params(**kw):
+    base = dict(B=1, H=1, Sq=16, Skv=16, D=128, softmax_scale=128 ** -0.5, p_elem=2, tau=8.0, schraudolph_c=0.0,
+                kv_tile=64, rollback_counts=None, p_dump_codes=None, p_dump_scales=None, p_b=0, p_h=0, p_row0=0,
+                p_row1=0)
+    base.update(kw)
+    return fs._Params(**base)
+
+
+def _mx(elem=2, prescale=None):
+    ps = fs.fold_prescale(128 ** -0.5) if prescale is None else prescale
+    return fs._MxTensor(elem, ps, 16, 16)  # fake aligned non-null pointers: validation only
+
+
+def _call(p, q, k, v, out=16):
+    return fs.lib().fsattn_forward(ctypes.byref(p), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out, None)
+
+
+def test_forward_validation_rejects_before_launch():
+    k1 = _mx(prescale=1.0)
+    v1 = _mx(prescale=1.0)
+    E = fs.lib()
+    assert E.fsattn_forward(None, None, None, None, None, None) == -1
+    assert _call(_params(D=96), _mx(), k1, v1) == -1                 # head dim
+    assert _call(_params(kv_tile=96), _mx(), k1, v1) == -1           # gate tile
+    assert _call(_params(tau=-1.0), _mx(), k1, v1) == -1             # tau
+    assert _call(_params(Skv=0), _mx(), k1, v1) == -1                # no keys
+    assert _call(_params(), _mx(prescale=3.0), k1, v1) == -1         # fold prescale mismatch
+    assert _call(_params(), _mx(elem=2), _mx(elem=4, prescale=1.0), v1) == -1  # Q/K formats differ
+    assert _call(_params(p_elem=4), _mx(), k1, v1) == -2             # FP4 P unsupported
+    assert _call(_params(p_elem=0), _mx(), k1, v1) == -2             # FP8 P needs FP8 V
+    assert _call(_params(p_dump_codes=16, p_dump_scales=16, p_row0=4, p_row1=2), _mx(), k1, v1) == -1
+    assert _call(_params(), _mx(), k1, v1, out=None) == -1
+    bad = fs._MxTensor(2, fs.fold_prescale(128 ** -0.5), 8, 16)      # misaligned codes
+    assert _call(_params(), bad, k1, v1) == -3
+    assert _call(_params(Sq=0), _mx(), k1, v1) == 0                  # empty: OK, no launch
+
+
+def test_quantize_validation():
+    Q = fs.lib().fsattn_quantize_mx
+    assert Q(16, 1, 4, 100, 100, 0, ctypes.c_float(1.0), 2, 0, 16, 16, None) == -1  # cols % 32
+    assert Q(16, 1, 4, 128, 64, 0, ctypes.c_float(1.0), 2, 0, 16, 16, None) == -1   # ld < cols
+    assert Q(16, 1, 4, 128, 128, 2, ctypes.c_float(1.0), 2, 0, 16, 16, None) == -1  # axis
+    assert Q(16, 1, 4, 128, 128, 0, ctypes.c_float(1.0), 7, 0, 16, 16, None) == -1  # elem
+    assert Q(16, 1, 4, 128, 128, 0, ctypes.c_float(1.0), 2, 5, 16, 16, None) == -1  # rule
+    assert Q(16, 1, 4, 128, 128, 0, ctypes.c_float(1.0), 2, 0, 8, 16, None) == -3   # codes alignment
+    assert Q(None, 1, 4, 128, 128, 0, ctypes.c_float(1.0), 2, 0, 16, 16, None) == -1
+    assert Q(None, 0, 4, 128, 128, 0, ctypes.c_float(1.0), 2, 0, None, None, None) == 0  # empty
+
+
+def test_bf16_baseline_validation():
+    B = fs.lib().fsattn_forward_bf16_baseline
+    assert B(16, 16, 16, 1, 1, 8, 8, 96, ctypes.c_float(0.1), 16, None) == -1
+    assert B(16, 16, 16, 1, 1, 8, 0, 128, ctypes.c_float(0.1), 16, None) == -1
+    assert B(8, 16, 16, 1, 1, 8, 8, 128, ctypes.c_float(0.1), 16, None) == -3
+    assert B(16, 16, 16, 1, 1, 0, 8, 128, ctypes.c_float(0.1), 16, None) == 0

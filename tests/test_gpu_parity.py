@@ -1,0 +1,75 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases span several 128-key tiles, ragged query and key tails, both
+head dimensions, every supported format combination, the rollback path
+(stress rows, tau = 0) and the no-rollback limit (tau huge); P codes are
+compared for a window of rows through the library's P dump.  The benchmark
+workloads follow at their full sizes: all rows for the two small ones, a
+seeded row sample (first and last row included) for the large ones, and the
+quantizer bytes on the full tensors.
+"""
+import pytest
+import torch
+
+from softmax_matrix_cores_amd import workloads as W
+from tests.gpu_util import assert_ok, run_case
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # name, base recipe, overrides
+    ("fp6-ragged", "qknorm-mxfp6", dict(B=1, H=2, Sq=200, Skv=333, D=128, seed=11)),
+    ("fp4-ragged", "qknorm-mxfp4", dict(B=2, H=1, Sq=130, Skv=515, D=128, seed=12)),
+    ("fp8-ragged", "stress-mxfp8", dict(B=1, H=2, Sq=97, Skv=300, D=128, seed=13)),
+    ("fp8-d64", "tiny-mxfp8", dict(B=1, H=2, Sq=70, Skv=190, D=64, seed=14)),
+    ("fp6-d64", "qknorm-mxfp6", dict(B=1, H=2, Sq=64, Skv=256, D=64, seed=15)),
+    ("fp6-stress", "stress-mxfp8", dict(B=1, H=2, Sq=128, Skv=640, D=128, seed=16, qk_elem="e2m3",
+                                        v_elem="e2m3", p_elem="e2m3")),
+    ("fp4-stress", "stress-mxfp8", dict(B=1, H=2, Sq=128, Skv=640, D=128, seed=17, qk_elem="e2m1",
+                                        v_elem="e2m1", p_elem="e2m3")),
+    ("fp6-skv1", "qknorm-mxfp6", dict(B=1, H=1, Sq=33, Skv=1, D=128, seed=18)),
+    ("fp8-skv40", "tiny-mxfp8", dict(B=1, H=1, Sq=20, Skv=40, D=128, seed=19)),
+]
+
+
+@pytest.mark.parametrize("name,base,kw", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("kv_tile", [64, 128])
+def test_small_cases(oracle, name, base, kw, kv_tile):
+    w = W.custom(base, name=name, **kw)
+    res = run_case(oracle, w, dump_head=(0, w.H - 1), dump_rows=(0, min(w.Sq, 40)), kv_tile=kv_tile)
+    assert_ok(res)
+
+
+@pytest.mark.parametrize("tau", [0.0, 2.0, 1e4])
+@pytest.mark.parametrize("elems", [("e2m3", "e2m3", "e2m3"), ("e4m3", "e4m3", "e4m3"), ("e2m1", "e2m1", "e2m3")])
+def test_tau_sweep(oracle, tau, elems):
+    qk, ve, pe = elems
+    w = W.custom("stress-mxfp8", name=f"tau{tau}-{qk}", B=1, H=2, Sq=96, Skv=520, D=128, seed=21, qk_elem=qk,
+                 v_elem=ve, p_elem=pe)
+    res = run_case(oracle, w, dump_head=(0, 1), dump_rows=(0, 32), tau=tau)
+    assert_ok(res)
+    if tau == 0.0:
+        assert res["total_counts"] > 0
+    if tau == 1e4:
+        assert res["total_counts"] == 0
+
+
+def test_tiny_mxfp8_full(oracle):
+    w = W.WORKLOADS["tiny-mxfp8"]
+    res = run_case(oracle, w, dump_head=(0, 1), dump_rows=(0, w.Sq))
+    assert_ok(res)
+
+
+def test_stress_mxfp8_full(oracle):
+    w = W.WORKLOADS["stress-mxfp8"]
+    res = run_case(oracle, w, dump_head=(0, 3), dump_rows=(0, w.Sq))
+    assert res["total_counts"] > 0
+    assert_ok(res)
+
+
+@pytest.mark.parametrize("name", ["qknorm-mxfp6", "qknorm-mxfp4", "video-mxfp6", "video-mxfp4"])
+def test_large_sampled(oracle, name):
+    w = W.WORKLOADS[name]
+    rows = W.sample_rows(w, 256).numpy()
+    res = run_case(oracle, w, rows=rows, dump_head=(w.B - 1, w.H - 1), dump_rows=(w.Sq - 8, w.Sq))
+    assert_ok(res)
