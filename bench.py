@@ -1,0 +1,245 @@
+"""Benchmark of the Fused-Softmax attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+MX-quantize Q (with the folded prescale), K and V, then the fused forward
+(scores with the folded reference, rollback gate, two-stage P, P V and P 1).
+Inputs are resident in HBM before timing starts.  Reported:
+
+  value        attention TFLOPS of the whole step, 4*B*H*S^2*D / step time
+  roofline     the fused-forward kernel against the MX matrix-core peak
+               (algorithmic flops 4*B*H*S^2*D per launch / mean launch time,
+               HIP events on the launch stream)
+  formats      kernel TFLOPS, MX-MFMA utilisation and speedup over the
+               in-library BF16 attention kernel for each format of the workload
+  cpu_baseline the CPU oracle on a bounded sample of query rows of the same
+               workload, in the same unit
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video-mxfp6]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOPS (4·H·S²·D) + MX-MFMA util %; speedup vs in-lib BF16 attn"
+# MI355X dense matrix-core peaks (TFLOP/s)
+PEAK = {"e4m3": 5000.0, "e2m3": 10100.0, "e2m1": 10100.0, "bf16": 2500.0}
+FWD_SRC = os.path.join(ROOT, "softmax_matrix_cores_amd", "csrc", "fsattn_fwd.hip")
+
+
+def _peak_for(w) -> float:
+    # a contraction takes the peak of its slowest operand format (P and V share the PV product)
+    fmts = {w.qk_elem, w.v_elem, w.p_elem}
+    return min(PEAK[f] for f in fmts)
+
+
+def _src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/), if they
+    were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"fsattn_fwd_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_src_sha256_16") != _src_hash(FWD_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_path(fs, W, w, q, k, v, steps, warmup):
+    """Time `steps` whole-path steps; returns (ms_per_step, fwd_ms_mean, quant_ms_mean, out, counts)."""
+    import torch
+
+    dev = q.device
+    st = torch.cuda.current_stream()
+    Q = fs.quantize_mx(q, 0, w.qk_elem, prescale=fs.fold_prescale(w.sigma))
+    K = fs.quantize_mx(k, 0, w.qk_elem)
+    V = fs.quantize_mx(v, 1, w.v_elem)
+    out = torch.empty(w.B, w.H, w.Sq, w.D, dtype=torch.bfloat16, device=dev)
+    counts = torch.zeros(w.B, w.H, w.Sq, dtype=torch.int32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(st)
+        fs.quantize_mx(q, 0, w.qk_elem, prescale=fs.fold_prescale(w.sigma), out=Q)
+        fs.quantize_mx(k, 0, w.qk_elem, out=K)
+        fs.quantize_mx(v, 1, w.v_elem, out=V)
+        if ev is not None:
+            ev[1].record(st)
+        fs.forward(Q, K, V, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=w.tau, kv_tile=w.kv_tile,
+                   counts=counts, out=out)
+        if ev is not None:
+            ev[2].record(st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(st)
+    for i in range(steps):
+        step(evs[i])
+    t1.record(st)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    fwd = [e[1].elapsed_time(e[2]) for e in evs]
+    qnt = [e[0].elapsed_time(e[1]) for e in evs]
+    return total / steps, sum(fwd) / len(fwd), max(fwd), sum(qnt) / len(qnt), out, counts
+
+
+def time_bf16(fs, w, q, k, v, steps, warmup):
+    import torch
+
+    st = torch.cuda.current_stream()
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        fs.forward_bf16_baseline(q, k, v, w.sigma, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(st)
+        fs.forward_bf16_baseline(q, k, v, w.sigma, out=out)
+        b.record(st)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in ev]
+    return sum(ts) / len(ts), out
+
+
+def cpu_baseline(w, q, k, v, budget_s: float = 15.0):
+    """The oracle on sampled query rows of one head, in attention TFLOPS."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    def bits(x):
+        return x.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    h = 0
+    qh, kh, vh = (x[0, h].cpu() for x in (q, k, v))
+    qk, ve, pe = O.ELEM_NAMES[w.qk_elem], O.ELEM_NAMES[w.v_elem], O.ELEM_NAMES[w.p_elem]
+    Qo = O.quantize_mx(bits(qh).reshape(1, w.Sq, w.D), 0, qk, prescale=O.softmax_scale_prescale(w.sigma))
+    Ko = O.quantize_mx(bits(kh).reshape(1, w.Skv, w.D), 0, qk)
+    Vo = O.quantize_mx(bits(vh).reshape(1, w.Skv, w.D), 1, ve)
+    p = O.make_params(1, 1, w.Sq, w.Skv, w.D, qk, ve, pe, tau=w.tau, kv_tile=w.kv_tile)
+    threads = O.lib().fso_default_threads()
+    gen = torch.Generator().manual_seed(7)
+    # calibrate on a few rows, then size the sample to the time budget
+    n0 = max(threads, 8)
+    rows = torch.randperm(w.Sq, generator=gen)[:n0].numpy().astype(np.int64)
+    t = time.perf_counter()
+    O.forward(p, Qo, Ko, Vo, rows=rows)
+    dt0 = time.perf_counter() - t
+    n = int(min(w.Sq, max(n0, n0 * budget_s / max(dt0, 1e-3))))
+    n = (n // threads) * threads or n0
+    rows = torch.randperm(w.Sq, generator=gen)[:n].numpy().astype(np.int64)
+    t = time.perf_counter()
+    O.forward(p, Qo, Ko, Vo, rows=rows)
+    dt = time.perf_counter() - t
+    flops = 4.0 * n * w.Skv * w.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows of head 0 of {w.name} (all {w.Skv} keys), fused forward only; "
+                      f"{dt:.1f} s wall, {flops / n:.3g} flop/row"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video-mxfp6")
+    ap.add_argument("--also", default="auto", help="other formats of the same shape (auto: the video pair)")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import softmax_matrix_cores_amd as fs
+    from softmax_matrix_cores_amd import workloads as W
+
+    if not os.path.exists(fs.LIB_PATH):
+        raise SystemExit("libfsattn.so is not built; run `python __graft_entry__.py build`")
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = W.make_inputs(w, device="cuda:0")
+    torch.cuda.synchronize()
+
+    variants = [w]
+    if args.also == "auto" and w.name.startswith("video-"):
+        variants += [W.WORKLOADS[n] for n in ("video-mxfp6", "video-mxfp4") if n != w.name]
+    elif args.also not in ("auto", "none", ""):
+        variants += [W.WORKLOADS[n] for n in args.also.split(",")]
+
+    bf16_ms = None
+    if not args.no_bf16:
+        print("[bench] bf16 baseline", file=sys.stderr, flush=True)
+        bf16_ms, _ = time_bf16(fs, w, q, k, v, max(3, args.steps // 2), 1)
+
+    formats = {}
+    main_res = None
+    for vw in variants:
+        print(f"[bench] fused {vw.name}", file=sys.stderr, flush=True)
+        st_ms, fwd_ms, fwd_max, q_ms, out, counts = time_path(fs, W, vw, q, k, v, args.steps if vw is w else
+                                                              max(3, args.steps // 2), args.warmup)
+        k_tflops = vw.flops / (fwd_ms * 1e-3) / 1e12
+        rec = {"kernel_tflops": round(k_tflops, 2), "kernel_ms": round(fwd_ms, 4), "kernel_ms_slowest": round(fwd_max, 4),
+               "quantize_ms": round(q_ms, 4), "step_ms": round(st_ms, 4),
+               "mx_mfma_util": round(k_tflops / _peak_for(vw), 4),
+               "rollbacks": int(counts.sum().item())}
+        if bf16_ms is not None:
+            rec["speedup_vs_bf16_kernel"] = round(bf16_ms / fwd_ms, 3)
+            rec["speedup_vs_bf16_incl_quant"] = round(bf16_ms / st_ms, 3)
+        formats[vw.name] = rec
+        if vw is w:
+            main_res = (st_ms, fwd_ms, rec)
+
+    st_ms, fwd_ms, rec = main_res
+    value = w.flops / (st_ms * 1e-3) / 1e12
+    achieved = w.flops / (fwd_ms * 1e-3) / 1e12
+    peak = _peak_for(w)
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(st_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"e2m3": "mxfp6", "e2m1": "mxfp4", "e4m3": "mxfp8"}[w.qk_elem],
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.Sq, "D": w.D, "qk": w.qk_elem, "v": w.v_elem,
+                   "p": w.p_elem, "tau": w.tau, "kv_tile": w.kv_tile},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": _traffic(w.name),
+                     "kernel": "fsattn_fwd_kernel", "flops_per_launch": w.flops},
+        "formats": formats,
+    }
+    if bf16_ms is not None:
+        line["bf16_baseline"] = {"kernel_ms": round(bf16_ms, 4),
+                                 "tflops": round(w.flops / (bf16_ms * 1e-3) / 1e12, 2),
+                                 "bf16_mfma_util": round(w.flops / (bf16_ms * 1e-3) / 1e12 / PEAK["bf16"], 4)}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

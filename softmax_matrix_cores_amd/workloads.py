@@ -20,9 +20,11 @@ an AI attention bottleneck onto faster GPU hardware", paragraphs 7-8):
                                           rank-16 positional term, V iid
 
 Recipe (fixed draw order so any consumer can regenerate it):
-  torch.Generator('cpu').manual_seed(seed); Q, K, V drawn as fp32 randn in
+  torch.Generator(device).manual_seed(seed); Q, K, V drawn as fp32 randn in
   that order, then the auxiliary draws; every tensor is cast to bf16 (RNE) at
   the end.  softmax scale sigma = 1/sqrt(D); non-causal; Sq = Skv = S.
+  Large workloads are drawn on the GPU (milliseconds instead of a minute);
+  the oracle then receives a host copy of the very same bf16 tensors.
 """
 from __future__ import annotations
 
@@ -81,25 +83,30 @@ def _rms_gain(x: torch.Tensor, gain: torch.Tensor) -> torch.Tensor:
     return x / torch.sqrt((x * x).mean(dim=-1, keepdim=True) + 1e-6) * gain.view(1, -1, 1, 1)
 
 
-def _video_features(n_tokens: int, rank: int, gen: torch.Generator) -> torch.Tensor:
+def _video_features(n_tokens: int, rank: int, gen: torch.Generator, device) -> torch.Tensor:
     """Seeded low-frequency random Fourier features of the latent grid, [S, rank]."""
     F, Y, X = VIDEO_GRID
-    s = torch.arange(n_tokens, dtype=torch.float64)
+    s = torch.arange(n_tokens, dtype=torch.float64, device=device)
     f = torch.div(s, Y * X, rounding_mode="floor")
     y = torch.div(s - f * Y * X, X, rounding_mode="floor")
     x = s - f * Y * X - y * X
     pos = torch.stack([f / F, y / Y, x / X], dim=1)  # [S, 3]
-    omega = torch.randint(-4, 5, (rank, 3), generator=gen).to(torch.float64)
-    phi = torch.rand(rank, generator=gen, dtype=torch.float64) * (2 * math.pi)
+    omega = torch.randint(-4, 5, (rank, 3), generator=gen, device=device).to(torch.float64)
+    phi = torch.rand(rank, generator=gen, dtype=torch.float64, device=device) * (2 * math.pi)
     return (math.sqrt(2.0) * torch.cos(2 * math.pi * (pos @ omega.T) + phi)).to(torch.float32)
 
 
-def make_inputs(w: Workload) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Q [B,H,Sq,D], K [B,H,Skv,D], V [B,H,Skv,D] as contiguous CPU bf16 tensors."""
-    gen = torch.Generator("cpu").manual_seed(w.seed)
-    q = torch.randn(w.B, w.H, w.Sq, w.D, generator=gen, dtype=torch.float32)
-    k = torch.randn(w.B, w.H, w.Skv, w.D, generator=gen, dtype=torch.float32)
-    v = torch.randn(w.B, w.H, w.Skv, w.D, generator=gen, dtype=torch.float32)
+def make_inputs(w: Workload, device="cpu") -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Q [B,H,Sq,D], K [B,H,Skv,D], V [B,H,Skv,D] as contiguous bf16 tensors on `device`.
+
+    The draws use a generator of that device seeded with w.seed, so a given
+    (workload, device type) always yields the same tensors; CPU and CUDA
+    draws differ from each other.  A comparison feeds both sides from one draw."""
+    device = torch.device(device)
+    gen = torch.Generator(device).manual_seed(w.seed)
+    q = torch.randn(w.B, w.H, w.Sq, w.D, generator=gen, dtype=torch.float32, device=device)
+    k = torch.randn(w.B, w.H, w.Skv, w.D, generator=gen, dtype=torch.float32, device=device)
+    v = torch.randn(w.B, w.H, w.Skv, w.D, generator=gen, dtype=torch.float32, device=device)
     if w.recipe == "iid":
         pass
     elif w.recipe == "stress":
@@ -107,20 +114,20 @@ def make_inputs(w: Workload) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
         n = max(1, round(0.01 * w.Skv))
         for b in range(w.B):
             for h in range(w.H):
-                rows = torch.randperm(w.Skv, generator=gen)[:n]
+                rows = torch.randperm(w.Skv, generator=gen, device=device)[:n]
                 k[b, h, rows] *= 8.0
     elif w.recipe in ("qknorm", "video"):
-        gq = torch.rand(w.H, generator=gen) * 1.5 + 0.5
-        gk = torch.rand(w.H, generator=gen) * 1.5 + 0.5
+        gq = torch.rand(w.H, generator=gen, device=device) * 1.5 + 0.5
+        gk = torch.rand(w.H, generator=gen, device=device) * 1.5 + 0.5
         q = _rms_gain(q, gq)
         k = _rms_gain(k, gk)
         if w.recipe == "video":
             rank = 16
             if w.Sq != w.Skv:
                 raise ValueError("video recipe needs Sq == Skv")
-            z = _video_features(w.Sq, rank, gen)  # [S, 16]
-            rq = torch.randn(w.H, rank, w.D, generator=gen) * 0.25  # N(0, 1/16)
-            rk = torch.randn(w.H, rank, w.D, generator=gen) * 0.25
+            z = _video_features(w.Sq, rank, gen, device)  # [S, 16]
+            rq = torch.randn(w.H, rank, w.D, generator=gen, device=device) * 0.25  # N(0, 1/16)
+            rk = torch.randn(w.H, rank, w.D, generator=gen, device=device) * 0.25
             for h in range(w.H):
                 q[:, h] += z @ rq[h]
                 k[:, h] += z @ rk[h]

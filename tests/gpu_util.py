@@ -71,7 +71,7 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
     Returns a dict of metrics; asserts nothing."""
     log(f"[case] {w.name} B={w.B} H={w.H} Sq={w.Sq} Skv={w.Skv} D={w.D} {w.qk_elem}/{w.v_elem}/{w.p_elem} "
         f"tau={w.tau if tau is None else tau} kv_tile={w.kv_tile if kv_tile is None else kv_tile}")
-    q, k, v = W.make_inputs(w)
+    q, k, v = (x.cpu() for x in W.make_inputs(w, device="cuda:0"))
     tau_ = w.tau if tau is None else tau
     kvt = w.kv_tile if kv_tile is None else kv_tile
     res = {}
