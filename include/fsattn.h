@@ -142,9 +142,9 @@ typedef struct {
  *
  * Per query row i and kv tile j (kv_tile keys, ascending):
  *   t = fl32(C_i + sum_d Qhat_id Khat_kd)   (tile 0: C_i = 0, then
- *       C_i = floor(T0 - max t), t += C_i; T0 = fl32(128*127 - c))
+ *       C_i = fl32(T0 - max t), t += C_i; T0 = fl32(128*127 - c))
  *   rollback: if max_k t > T_gate = fl32(128*(127+tau) - c) (tiles j >= 1),
- *       delta = ceil(max t - T0); t -= delta; C_i -= delta;
+ *       delta = fl32(max t - T0); t -= delta; C_i -= delta;
  *       O_i, l_i *= 2^(-delta/128); count_i += 1
  *   stage 1: b = floor(t) as a BF16 bit pattern (0 if t < 128, at most 0x7F7F)
  *   stage 2: P = MX(bf16(b)) per 32 consecutive keys (fit-max E8M0)

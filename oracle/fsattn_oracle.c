@@ -23,13 +23,10 @@
  *
  *  Readings where the pages are silent (the oracle's contract):
  *   R1  tau is in log2 units of P: tile fires when max score > reference + tau.
- *   R2  initial reference = row max of the first kv tile, not counted.  The
- *       reference is kept on the integer grid of the BF16 bit pattern (1/128
- *       of a log2 unit): C_i = floor(T0 - tmax), so the row max maps to a
- *       pattern within one unit below T0 (P <= 2^(-c/128)) and C_i is an
- *       integer.
- *   R3  on a fire, the new reference is that tile's row max, again on the
- *       grid: delta = ceil(tmax - T0), an integer.
+ *   R2  initial reference = row max of the first kv tile, not counted:
+ *       C_i = fl32(T0 - tmax), so the row max maps to T0 (P = 2^(-c/128)).
+ *   R3  on a fire, the new reference is that tile's row max:
+ *       delta = fl32(tmax - T0), C_i = fl32(C_i - delta).
  *   R4  gate per row, per kv_tile keys, strict '>', valid keys only.
  *   R5  correction multiplies O and l by exactly 2^(-delta/128).
  *   R6  Schraudolph shift c (default 0) in BF16-pattern units.
@@ -610,17 +607,16 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
       if (t > tmax) tmax = t;
     }
     if (j == 0) {
-      /* frozen reference on the BF16-pattern integer grid (R2): the row max
-       * maps to at most T0 */
-      C = floor(exact ? (T0 - tmax) : (double)(float)(T0 - tmax));
+      /* frozen reference (R2): the row max maps to T0 */
+      C = exact ? (T0 - tmax) : (double)(float)(T0 - tmax);
       for (int64_t k = k0; k < k1; ++k) rb->tmp[k] = exact ? rb->tmp[k] + C : (double)(float)(rb->tmp[k] + C);
     } else if (tmax > Tg) {
-      /* rollback gate (R1, R3, R4, R5) [FS-news 5]: integer shift that brings
-       * this tile's max back to at most T0 */
-      double delta = ceil(exact ? (tmax - T0) : (double)(float)(tmax - T0));
+      /* rollback gate (R1, R3, R4, R5) [FS-news 5]: shift that brings this
+       * tile's max back to T0 */
+      double delta = exact ? (tmax - T0) : (double)(float)(tmax - T0);
       for (int64_t k = k0; k < k1; ++k)
         rb->tmp[k] = exact ? rb->tmp[k] - delta : (double)(float)(rb->tmp[k] - delta);
-      C = C - delta; /* integers: exact */
+      C = exact ? C - delta : (double)(float)(C - delta);
       double rho = exp2(-delta / 128.0);
       for (int d = 0; d < D; ++d) O[d] *= rho;
       l *= rho;
@@ -693,8 +689,6 @@ static void reference_row(job_t* J, int64_t ri, rowbuf_t* rb) {
       int64_t kb1 = (k1 == Skv) ? S32 : k1;
       double mt = -INFINITY;
       for (int64_t k = k0; k < k1; ++k) if (rb->tmp[k] > mt) mt = rb->tmp[k];
-      /* running max kept on the 1/128-log2 grid, rounded up */
-      mt = ceil(mt * 128.0) / 128.0;
       double mnew = mt > mrun ? mt : mrun;
       if (mrun != -INFINITY && mnew > mrun) {
         double r = exp2(mrun - mnew);

@@ -56,8 +56,7 @@ enum {
   FSO_REF_R1 = 1,   /* exact softmax of the quantized scores, V-hat, P unquantized */
   FSO_REF_R2 = 2,   /* conventional softmax, numerator uses MX-quantized p, denominator sum p */
   FSO_REF_R2P = 3,  /* as R2 but denominator sum of MX-quantized p */
-  FSO_REF_R3 = 4    /* FlashAttention online max/rescale per kv tile (running max rounded up to
-                       the 1/128-log2 grid), MX-quantized p in both sums */
+  FSO_REF_R3 = 4    /* FlashAttention online max/rescale per kv tile, MX-quantized p in both sums */
 };
 
 #define FSO_OK 0

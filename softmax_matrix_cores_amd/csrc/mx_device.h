@@ -23,6 +23,7 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v6i __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned v16u __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v2s __attribute__((ext_vector_type(2)));

@@ -181,15 +181,15 @@ def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, ta
             ks = list(range(j * kv_tile, min((j + 1) * kv_tile, Skv)))
             if j == 0:
                 t = {k: fl32(sig[k]) for k in ks}
-                C = Fraction(math.floor(fl32(T0 - max(t.values()))))
+                C = fl32(T0 - max(t.values()))
                 t = {k: fl32(t[k] + C) for k in ks}
             else:
                 t = {k: fl32(C + sig[k]) for k in ks}
                 mx = max(t.values())
                 if mx > Tg:
-                    delta = Fraction(math.ceil(fl32(mx - T0)))
+                    delta = fl32(mx - T0)
                     t = {k: fl32(t[k] - delta) for k in ks}
-                    C -= delta
+                    C = fl32(C - delta)
                     rho = 2.0 ** (-float(delta) / 128.0)
                     num = [x * Fraction(rho) for x in num]
                     den = den * Fraction(rho)

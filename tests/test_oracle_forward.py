@@ -228,8 +228,8 @@ def test_I5_planted_overshoot(oracle):
     # hand value of the shift: folded scores are exact here (E2M3 grid), t_max(tile1) - T0
     s = [oracle.folded_score(2, Q[0][0, 0], Q[1][0, 0], K[0][0, kk], K[1][0, kk], D, 0.0, exact=True)
          for kk in range(64)]
-    C = math.floor(16256.0 - max(s[:32]))
-    delta = math.ceil(max(s[32:]) + C - 16256.0)
+    C = 16256.0 - max(s[:32])
+    delta = max(s[32:]) + C - 16256.0
     assert delta >= 128 * tau
     # O after the fire equals the spec (which applies the same hand-derivable steps)
     O_s, cnt_s, _, _ = spec.forward(bits(q[0, 0]), bits(k[0, 0]), bits(v[0, 0]), sigma, 2, 2, 2, tau=tau,
