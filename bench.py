@@ -166,6 +166,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration for profiles)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -181,6 +183,14 @@ def main():
     if not os.path.exists(fs.LIB_PATH):
         raise SystemExit("libfsattn.so is not built; run `python __graft_entry__.py build`")
     torch.cuda.set_device(0)
+    if args.copy_calib_mib > 0:
+        # a plain copy kernel of known size: reads and writes copy_calib_mib MiB each
+        src = torch.ones(args.copy_calib_mib << 18, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = W.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = W.make_inputs(w, device="cuda:0")
