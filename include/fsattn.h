@@ -76,11 +76,16 @@ const char* fsattn_status_str(int status);
  * block_axis 0 (Q, K: blocks along the feature dimension):
  *   input  [n_mat][rows][cols] bf16 (row stride ld elements), cols % 32 == 0
  *   codes  [n_mat][rows][cols/32][block bytes]
- *   scales [n_mat][rows][cols/32]
+ *   scales [n_mat][rows][cols/32], followed by up to 3 bytes of padding
+ *          (fsattn_mx_scales_bytes rounds up to whole dwords; the forward
+ *          reads K scales a dword at a time)
  * block_axis 1 (V: blocks along keys), stored transposed, key-contiguous:
- *   input  [n_mat][rows][cols] bf16, rows = keys, cols = features
- *   codes  [n_mat][cols][rows32/32][block bytes], rows32 = rows rounded up to 32
- *   scales [n_mat][cols][rows32/32]; keys >= rows are zero padding.
+ *   input  [n_mat][rows][cols] bf16, rows = keys, cols = features (cols <= 128)
+ *   codes  [n_mat][cols][rows32/32][block bytes], rows32 = rows rounded up to 32;
+ *          keys >= rows are zero padding
+ *   scales [n_mat][rows32/32][32][4]: the scale of column c, key block b is at
+ *          [b][c % 32][c / 32] (bytes of absent columns are left unwritten), so
+ *          one dword holds the scales of columns c, c+32, c+64, c+96.
  */
 int64_t fsattn_mx_codes_bytes(int elem, int64_t n_mat, int64_t rows, int64_t cols, int block_axis);
 int64_t fsattn_mx_scales_bytes(int64_t n_mat, int64_t rows, int64_t cols, int block_axis);
@@ -101,8 +106,8 @@ int64_t fsattn_mx_scales_bytes(int64_t n_mat, int64_t rows, int64_t cols, int bl
  *  the element format (sign of zero kept).  Results are bit-exact with the
  *  definition above.  NaN/Inf inputs are outside the contract.
  *  Errors: FSATTN_E_INVALID_ARG (null, negative sizes, cols % 32 != 0 on
- *  axis 0, ld < cols, bad enum), FSATTN_E_ALIGNMENT (src, codes_out or
- *  scales_out not 16-byte aligned), FSATTN_E_HIP.
+ *  axis 0, cols > 128 on axis 1, ld < cols, bad enum), FSATTN_E_ALIGNMENT
+ *  (src not 2-byte or codes_out not 16-byte aligned), FSATTN_E_HIP.
  */
 int fsattn_quantize_mx(const void* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld, int block_axis,
                        float prescale, int elem, int rule, void* codes_out, uint8_t* scales_out, void* stream);
@@ -151,7 +156,9 @@ typedef struct {
  *   O_i += P V, l_i += P 1 (same P); finally O_i / l_i rounded to bf16.
  * Errors: FSATTN_E_INVALID_ARG (null, sizes, D not 64/128, kv_tile not
  * 64/128, tau < 0, prescale/softmax_scale mismatch, bad dump window),
- * FSATTN_E_UNSUPPORTED (format combination), FSATTN_E_ALIGNMENT, FSATTN_E_HIP.
+ * FSATTN_E_UNSUPPORTED (format combination, Skv * D > 2^30),
+ * FSATTN_E_ALIGNMENT (codes not 16-byte, K or V scales not 4-byte, out not
+ * 4-byte aligned), FSATTN_E_HIP.
  */
 int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsattn_mx_tensor* k,
                    const fsattn_mx_tensor* v, void* out, void* stream);

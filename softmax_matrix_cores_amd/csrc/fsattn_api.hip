@@ -69,7 +69,11 @@ int64_t fsattn_mx_codes_bytes(int elem, int64_t n_mat, int64_t rows, int64_t col
 int64_t fsattn_mx_scales_bytes(int64_t n_mat, int64_t rows, int64_t cols, int block_axis) {
   if (n_mat < 0 || rows < 0 || cols < 0 || (block_axis != 0 && block_axis != 1)) return -1;
   if (block_axis == 0 && cols % 32) return -1;
-  return nblocks(n_mat, rows, cols, block_axis);
+  if (block_axis == 1) {
+    if (cols > 128) return -1;
+    return n_mat * ((rows + 31) / 32) * 128;  // [n_mat][blocks][32][4], see the header
+  }
+  return (nblocks(n_mat, rows, cols, block_axis) + 3) & ~(int64_t)3;  // padded to whole dwords
 }
 
 int fsattn_quantize_mx(const void* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld, int block_axis,
@@ -78,6 +82,7 @@ int fsattn_quantize_mx(const void* src, int64_t n_mat, int64_t rows, int64_t col
   if (block_axis != 0 && block_axis != 1) return FSATTN_E_INVALID_ARG;
   if (n_mat < 0 || rows < 0 || cols < 0 || ld < cols) return FSATTN_E_INVALID_ARG;
   if (block_axis == 0 && cols % 32) return FSATTN_E_INVALID_ARG;
+  if (block_axis == 1 && cols > 128) return FSATTN_E_INVALID_ARG;
   if (!isfinite(prescale)) return FSATTN_E_INVALID_ARG;
   if (n_mat == 0 || rows == 0 || cols == 0) return FSATTN_OK;
   if (!src || !codes_out || !scales_out) return FSATTN_E_INVALID_ARG;
@@ -114,6 +119,9 @@ int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsat
     return FSATTN_E_INVALID_ARG;
   if (!aligned(q->codes, 16) || !aligned(k->codes, 16) || !aligned(v->codes, 16) || !aligned(out, 4))
     return FSATTN_E_ALIGNMENT;
+  if (!aligned(k->scales, 4) || !aligned(v->scales, 4)) return FSATTN_E_ALIGNMENT;
+  // per-head byte counts of the K and V codes must fit the 32-bit buffer range
+  if ((int64_t)p->Skv * p->D > ((int64_t)1 << 30)) return FSATTN_E_UNSUPPORTED;
   fsattn::FwdArgs a;
   a.qc = static_cast<const uint8_t*>(q->codes);
   a.qs = q->scales;

@@ -6,7 +6,7 @@
 //   * the row-max reference is provisionally frozen; its subtraction and the
 //     affine part of Schraudolph's exponential are folded into the Q K^T
 //     product: the slope (128 log2 e sigma) sits in Q-hat, the offset
-//     C_i = T0 - m_i is the accumulator's initial value of the MFMA;
+//     C_i = T0 - m_i is the accumulator's initial value of the matrix op;
 //   * stage 1: the integer part of the folded score is the BF16 bit pattern
 //     of ~2^(score - m); stage 2: BF16 -> MX P with one E8M0 per 32 keys;
 //   * O += P V and l += P 1 run on the matrix cores with the same P;
@@ -14,724 +14,754 @@
 //     than tau: the reference is raised and O, l are rescaled.
 //
 // Mapping to CDNA4:
-//   * v_mfma_scale_f32_16x16x128_f8f6f4 for every product.  D = 128 is one
-//     contraction, so the fold C + sum Q K is a single instruction; with FP6
-//     and FP4 operands C_i lies on the grid of the scores and the sum is exact.
-//   * S^T = K Q^T: the accumulator's rows are keys, its columns queries, so a
-//     lane holds 32 scores of ONE query.  The K rows fed to each of the 8
-//     MFMAs of a 128-key tile are permuted so that those 32 scores are exactly
-//     the keys of the lane's P operand in the PV product: no transpose.
-//   * a wave owns NQ blocks of 16 queries; every K and V operand read from LDS
-//     feeds NQ MFMAs.  K/V tiles of 128 keys are double-buffered in LDS and
-//     fetched with direct global->LDS loads while the previous tile computes.
+//   * 8 waves per workgroup (two per SIMD), 32 queries per wave.  With two
+//     resident waves a SIMD overlaps one wave's softmax VALU work with the
+//     other's matrix instructions.
+//   * keys advance in steps of 64, one gate tile.  Every product is
+//     v_mfma_scale_f32_32x32x64_f8f6f4: S^T = K Q^T (2 key groups x D/64
+//     feature halves, the fold offset C_i as the accumulator's initial value),
+//     O += P V (D/32 feature blocks).  l += P 1 uses one 16x16x128
+//     instruction whose ones operand selects, per output column, the lanes of
+//     one query (FP6 P), or a 32x32x64 ones operand (FP8 P).
+//   * the K rows of the score instructions are permuted so that a lane's 32
+//     scores are exactly the 32 keys of its P operand in the PV product.
+//   * step u issues its score product and the PV product of step u-1 on the
+//     matrix cores, then converts the scores of step u on the VALU while the
+//     PV instructions run.
+//   * K and V operands sit in an 8-slot LDS ring in operand order, so every
+//     operand read is a lane-contiguous ds_read_b128 (plus a ds_read_b64 for
+//     the last 8 bytes of an FP6 lane): no bank conflicts.  The ring is
+//     filled six steps ahead by buffer_load ... lds DMA with constant per-lane
+//     offsets; the step moves the buffer descriptor, so reads past the end of
+//     K or V return zeros.
+//   * scales: one dword per key holds its K block scales; V scales come in the
+//     quantizer's interleaved layout, one dword per lane holding the scales of
+//     its PV instructions, picked with op_sel.
 //   * fast path per score: one float->int convert (stage 1), half a pack and
-//     half a max3; the E8M0 of P comes from the block max with integer
-//     exponent arithmetic and the whole 32-key block is converted by one
-//     v_cvt_scalef32_pk32_fp6_bf16.  A wave ballot on the block maxima sends
-//     a tile to the exact rare path when a gate might fire, when a block sits
-//     so low that the BF16 subnormal flush could matter, or on tile 0.
+//     half a max3.  The E8M0 of P comes from the block max with integer
+//     exponent arithmetic; one v_cvt_scalef32_pk32_fp6_bf16 converts a lane's
+//     32 keys.  A wave ballot sends a step to the exact path on the first
+//     step, a partial last step, a possible gate fire or stage-1 clamp, or a
+//     block low enough that the BF16 subnormal flush could change a code.
 //
-// Operand lane layouts of the scaled MFMA (measured on gfx950):
-//   FP6/FP4 ("contiguous"): lane (r = l%16, g = l/16) holds row r, K elements
-//     [32g, 32g+32) and the scale of that 32-block.
-//   FP8 ("split"): lane (r, g) holds K elements [16g, 16g+16) in bytes 0-15
-//     and [64+16g, 64+16g+16) in bytes 16-31; the scale of 32-block b comes
-//     from lane 16b + r.
-//   Accumulator: lane (n = l%16, g) holds rows 4g..4g+3 of column n.
+// Operand lane layouts of the 32x32x64 scaled MFMA (measured on gfx950):
+//   FP6/FP4: lane (r = l%32, h = l/32) holds row r, K elements [32h, 32h+32)
+//     and the scale of that 32-block.
+//   FP8: lane (r, h) holds K elements [16h, 16h+16) in bytes 0-15 and
+//     [32+16h, 32+16h+16) in bytes 16-31; the scale of block b comes from
+//     lane 32b + r.
+//   Accumulator: lane (c = l%32, h) register 4i+j holds row 8i+4h+j of
+//     column c.
 #include "internal.h"
 #include "mx_device.h"
 
 namespace fsattn {
+namespace {
 
-template <int ELEM> struct Layout { static constexpr bool split = (Fmt<ELEM>::bits == 8); };
+constexpr int NW = 8;         // waves per workgroup
+constexpr int QW = 32;        // queries per wave
+constexpr int QWG = NW * QW;  // queries per workgroup
+constexpr int KS = 64;        // keys per step
+constexpr int NS = 8;         // LDS ring slots
+constexpr int PF = NS - 2;    // steps fetched ahead
+constexpr int RSRC_W3 = 0x00020000;
 
-// V tile rows in LDS: 4 blocks of 32 keys.  A 24-byte FP6 block is stored as
-// two 12-byte halves at offsets 0 and 16 of a 32-byte slot, the placement of a
-// 12-byte direct global->LDS load (each lane's data lands on a 16-byte stride).
-template <int VELEM> struct VRowLds {
-  static constexpr int block = (Fmt<VELEM>::bits == 6) ? 32 : Fmt<VELEM>::bits * 4;
-  static constexpr int bytes = 4 * block;
+template <int F> struct Opd {
+  static constexpr int bits = Fmt<F>::bits;
+  static constexpr bool split = (bits == 8);
+  static constexpr int tail = 4 * bits - 16;  // bytes after the first 16 of a lane: 16, 8, 0
+  static constexpr int region = 64 * 4 * bits;
 };
 
-constexpr int NW = 4;    // waves per workgroup (one per SIMD)
-constexpr int KT = 128;  // keys per tile
-#ifndef FSATTN_LDS_DIRECT
-#define FSATTN_LDS_DIRECT 1  // K/V codes by direct global->LDS loads (else through registers)
-#endif
-#ifndef FSATTN_NQ
-#define FSATTN_NQ 2  // q-blocks of 16 queries per wave
-#endif
+template <int QK, int VE, int D> struct Geo {
+  static constexpr int DH = D / 64;  // feature halves of a score product
+  static constexpr int NK = 2 * DH;  // K operands per step
+  static constexpr int NV = D / 32;  // V operands per step
+  static constexpr int QRB = D * Fmt<QK>::bits / 8;
+  static constexpr int VBB = 4 * Fmt<VE>::bits;
+  static constexpr int KSB = D / 32;
+  static constexpr int K_OFF = 0;
+  static constexpr int KS_OFF = NK * Opd<QK>::region;
+  static constexpr int V_OFF = KS_OFF + 256;
+  static constexpr int VS_OFF = V_OFF + NV * Opd<VE>::region;
+  static constexpr int SLOT = VS_OFF + 256;
+  // DMA instructions per step with 16-byte and 4-byte lanes
+  static constexpr int N16 = NK + NV + (Opd<QK>::tail == 16 ? NK : 0) + (Opd<VE>::tail == 16 ? NV : 0);
+  static constexpr int N4 = (Opd<QK>::tail == 8 ? 2 * NK : 0) + (Opd<VE>::tail == 8 ? 2 * NV : 0) + 2;
+  static constexpr int M16 = (N16 + NW - 1) / NW;
+  static constexpr int M4 = (N4 + NW - 1) / NW;
+};
 
-template <int ELEM> __device__ __forceinline__ constexpr int block_bytes() { return Fmt<ELEM>::bits * 4; }
+// key (0..63 in the step) of accumulator register k (0..15) of key group kg, lane half h
+template <int PE> __device__ __forceinline__ constexpr int step_key(int kg, int k, int h) {
+  return Opd<PE>::split ? 32 * kg + 16 * h + k : 32 * h + 16 * kg + k;
+}
+// key fed to row rho (0..31) of the K operand of key group kg
+template <int PE> __device__ __forceinline__ constexpr int row_key(int kg, int rho) {
+  return step_key<PE>(kg, 4 * (rho >> 3) + (rho & 3), (rho >> 2) & 1);
+}
 
 // Smallest BF16 pattern of a P block max for which BF16 subnormals of the
 // block convert to +0 anyway (x/X at most half the format's smallest
-// subnormal): exponent field >= 7 (E2M3), 10 (E3M2), 19 (E4M3).
+// subnormal): exponent field >= 7 (E2M3), 19 (E4M3).
 template <int PELEM> struct PFlush;
 template <> struct PFlush<E2M3> { static constexpr float t = 896.0f; };
-template <> struct PFlush<E3M2> { static constexpr float t = 1280.0f; };
 template <> struct PFlush<E4M3> { static constexpr float t = 2432.0f; };
 
-// a lane's 32 K elements of a row laid out as consecutive 32-element blocks
-template <int ELEM, int D>
-__device__ __forceinline__ v8i load_row_operand(const uint8_t* row, int g) {
-  v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-  if constexpr (Layout<ELEM>::split) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * g);
-    a[0] = lo.x; a[1] = lo.y; a[2] = lo.z; a[3] = lo.w;
-    if constexpr (D == 128) {
-      const uint4 hi = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
-      a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
-    }
-  } else {
-    constexpr int BB = block_bytes<ELEM>();
-    if (D == 128 || g < 2) {
-      const uint8_t* p = row + BB * g;
-      if constexpr (BB == 24) {
-        const uint2* p2 = reinterpret_cast<const uint2*>(p);
-        uint2 x0 = p2[0], x1 = p2[1], x2 = p2[2];
-        a[0] = x0.x; a[1] = x0.y; a[2] = x1.x; a[3] = x1.y; a[4] = x2.x; a[5] = x2.y;
-      } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(p);
-        a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
-      }
-    }
-  }
-  return a;
-}
-
-// a lane's V operand (32 keys of one d row) from the LDS tile row
-template <int VELEM>
-__device__ __forceinline__ v8i load_v_operand(const uint8_t* row, int g) {
-  if constexpr (Fmt<VELEM>::bits == 6) {
-    const uint8_t* p = row + 32 * g;
-    const uint4 lo = *reinterpret_cast<const uint4*>(p);
-    const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)hi.x, (int)hi.y, (int)hi.z, 0, 0};
-  } else {
-    return load_row_operand<VELEM, 128>(row, g);
-  }
-}
-
 __device__ __forceinline__ float wshfl(float v, int src) { return __shfl(v, src, 64); }
-__device__ __forceinline__ int wshfl(int v, int src) { return __shfl(v, src, 64); }
 
-// key (0..127 in the tile) of accumulator j, row r' of lane group g
-template <int PELEM>
-__device__ __forceinline__ constexpr int key_of(int j, int rr, int g) {
-  if constexpr (Layout<PELEM>::split) return (j < 4) ? (16 * g + 4 * j + rr) : (64 + 16 * g + 4 * (j - 4) + rr);
-  else return 32 * g + 4 * j + rr;
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// 64-key gate half of accumulator j for lane group g
-template <int PELEM>
-__device__ __forceinline__ constexpr int half_of(int j, int g) {
-  if constexpr (Layout<PELEM>::split) return j >> 2;
-  else return g >> 1;
+// Wait until this wave's DMA of the oldest needed step has landed: with a
+// full pipeline PF-2 younger steps (n loads each) may still be in flight,
+// otherwise wait for everything.
+__device__ __forceinline__ void wait_steps(int n, bool full) {
+  if (!full) { wait_vm<0>(); return; }
+  switch (n) {
+    case 0: break;
+    case 1: wait_vm<(PF - 2) * 1>(); break;
+    case 2: wait_vm<(PF - 2) * 2>(); break;
+    case 3: wait_vm<(PF - 2) * 3>(); break;
+    case 4: wait_vm<(PF - 2) * 4>(); break;
+    case 5: wait_vm<(PF - 2) * 5>(); break;
+    default: wait_vm<0>(); break;
+  }
 }
 
-// Stage 1 with the flush and clamp (rare path): BF16 bit pattern of the
-// folded score.  v_cvt_u32_f32 truncates toward zero = floor for t >= 0.
-__device__ __forceinline__ uint32_t stage1_exact(float t) {
-  if (!(t >= 128.0f)) return 0u;
-  return min(__float2uint_rz(t), 0x7F7Fu);
+// workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding DMA); the clobber keeps LDS reads below it
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Buffer descriptor (raw, stride 0) of `bytes` bytes at `base`, in SGPRs.
+// Reads at or beyond `bytes` return zeros.
+__device__ __forceinline__ v4i rsrc(const uint8_t* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const int nrec = bytes <= 0 ? 0 : (int)bytes;
+  return v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)b), (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu),
+             __builtin_amdgcn_readfirstlane(nrec), RSRC_W3};
+}
+
+// buffer_load ... lds: each lane's 16 (or 4) bytes at voff land in LDS at
+// lds + 16 (or 4) * lane.  Issued as inline asm so that the compiler does not
+// treat the asynchronous LDS write as aliasing every later LDS read (it would
+// wait for all outstanding loads before each one); completion is tracked
+// explicitly with s_waitcnt vmcnt and published with s_barrier.
+// M0 (the LDS destination) is saved and restored around the instruction.
+__device__ __forceinline__ void dma_x4(const v4i& rs, uint32_t lds, int voff) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds), "v"(voff), "s"(rs));
+}
+__device__ __forceinline__ void dma_x1(const v4i& rs, uint32_t lds, int voff) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds), "v"(voff), "s"(rs));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// One lane's MFMA operand from an LDS region in operand order
+template <int F> __device__ __forceinline__ v8i lds_operand(const uint8_t* region, int lane) {
+  const uint4 x = *reinterpret_cast<const uint4*>(region + 16 * lane);
+  if constexpr (Opd<F>::tail == 16) {
+    const uint4 y = *reinterpret_cast<const uint4*>(region + 1024 + 16 * lane);
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  } else if constexpr (Opd<F>::tail == 8) {
+    const uint2 y = *reinterpret_cast<const uint2*>(region + 1024 + 8 * lane);
+    // keep the compiler from pairing this 8-byte read with another operand's
+    // into one ds_read2 (the halves would then need moves into the operand)
+    asm volatile("" ::: "memory");
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, 0, 0};
+  } else {
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+  }
+}
+
+// byte offsets (from the start of the head's K rows / V^T rows) of the two
+// chunks of a lane's K operand and V operand
+template <int QK, int D> __device__ __forceinline__ void k_chunks(int key, int dh, int hh, int& a, int& b) {
+  constexpr int QRB = D * Fmt<QK>::bits / 8;
+  if constexpr (Opd<QK>::split) {
+    a = key * QRB + 64 * dh + 16 * hh;
+    b = a + 32;
+  } else {
+    a = key * QRB + (2 * dh + hh) * (4 * Fmt<QK>::bits);
+    b = a + 16;
+  }
+}
+template <int VE> __device__ __forceinline__ void v_chunks(int d, int nb32, int hh, int& a, int& b) {
+  if constexpr (Opd<VE>::split) {
+    a = (d * nb32) * 32 + 16 * hh;
+    b = a + 32;
+  } else {
+    a = (d * nb32 + hh) * (4 * Fmt<VE>::bits);
+    b = a + 16;
+  }
+}
+
+// DMA item of a step: source buffer (base, size, bytes per step), LDS offset
+// in the slot, per-lane byte offset.  All but voff are wave-uniform.
+struct Dma {
+  const uint8_t* base;
+  int64_t bytes;
+  int stride;
+  int lds;
+  int voff;
+};
+
+template <int QK, int VE, int PE, int D>
+struct DmaSrc {
+  const uint8_t *k, *ks, *v, *vs;
+  int64_t kb, ksb, vb, vsb;
+  int ko;  // D = 64: the head's first key scale sits in the upper half of a dword
+  __device__ Dma kc(int lds, int voff) const { return Dma{k, kb, KS * (D * Fmt<QK>::bits / 8), lds, voff}; }
+  __device__ Dma vc(int lds, int voff) const { return Dma{v, vb, 2 * 4 * Fmt<VE>::bits, lds, voff}; }
+  __device__ Dma ksc(int lds, int voff) const { return Dma{ks, ksb, KS * (D / 32), lds, voff}; }
+  __device__ Dma vsc(int lds, int voff) const { return Dma{vs, vsb, 256, lds, voff}; }
+};
+
+template <int QK, int VE, int PE, int D>
+__device__ Dma dma16(int item, int lane, int nb32, const DmaSrc<QK, VE, PE, D>& src) {
+  using G = Geo<QK, VE, D>;
+  const int hh = lane >> 5, rho = lane & 31;
+  int a, b;
+  if (item < G::NK) {
+    const int kg = item / G::DH, dh = item % G::DH;
+    k_chunks<QK, D>(row_key<PE>(kg, rho), dh, hh, a, b);
+    return src.kc(G::K_OFF + item * Opd<QK>::region, a);
+  }
+  if (item < G::NK + G::NV) {
+    const int o = item - G::NK;
+    v_chunks<VE>(32 * o + rho, nb32, hh, a, b);
+    return src.vc(G::V_OFF + o * Opd<VE>::region, a);
+  }
+  int it = item - G::NK - G::NV;
+  if constexpr (Opd<QK>::tail == 16) {
+    if (it < G::NK) {
+      const int kg = it / G::DH, dh = it % G::DH;
+      k_chunks<QK, D>(row_key<PE>(kg, rho), dh, hh, a, b);
+      return src.kc(G::K_OFF + it * Opd<QK>::region + 1024, b);
+    }
+    it -= G::NK;
+  }
+  v_chunks<VE>(32 * it + rho, nb32, hh, a, b);
+  return src.vc(G::V_OFF + it * Opd<VE>::region + 1024, b);
+}
+
+template <int QK, int VE, int PE, int D>
+__device__ Dma dma4(int item, int lane, int nb32, const DmaSrc<QK, VE, PE, D>& src) {
+  using G = Geo<QK, VE, D>;
+  int it = item;
+  int a, b;
+  if constexpr (Opd<QK>::tail == 8) {
+    if (it < 2 * G::NK) {
+      // 8-byte tail of consumer lane L = 32p + (lane >> 1), dword lane & 1
+      const int o = it >> 1, p = it & 1, L = 32 * p + (lane >> 1);
+      const int kg = o / G::DH, dh = o % G::DH;
+      k_chunks<QK, D>(row_key<PE>(kg, L & 31), dh, L >> 5, a, b);
+      return src.kc(G::K_OFF + o * Opd<QK>::region + 1024 + 256 * p, b + 4 * (lane & 1));
+    }
+    it -= 2 * G::NK;
+  }
+  if constexpr (Opd<VE>::tail == 8) {
+    if (it < 2 * G::NV) {
+      const int o = it >> 1, p = it & 1, L = 32 * p + (lane >> 1);
+      v_chunks<VE>(32 * o + (L & 31), nb32, L >> 5, a, b);
+      return src.vc(G::V_OFF + o * Opd<VE>::region + 1024 + 256 * p, b + 4 * (lane & 1));
+    }
+    it -= 2 * G::NV;
+  }
+  if (it == 0) {
+    // K scales: lane i = 32 kg + rho loads the scale dword of its key
+    const int key = row_key<PE>(lane >> 5, lane & 31) + src.ko;
+    return src.ksc(G::KS_OFF + 4 * lane, (D == 128) ? key * 4 : (key & ~1) * 2);
+  }
+  return src.vsc(G::VS_OFF + 4 * lane, 4 * lane);
 }
 
 // E8M0 of a P block from its largest BF16 pattern (integer exponent math)
 template <int PELEM>
-__device__ __forceinline__ uint32_t p_scale(uint32_t bmax, bool fitmax) {
+__device__ __forceinline__ uint32_t p_scale(uint32_t bmax) {
   constexpr int thr7 = (int)(Fmt<PELEM>::mthr23 >> 16);  // 7-bit mantissa threshold
-  const int e = fitmax ? (int)((bmax + (uint32_t)(127 - thr7)) >> 7) : (int)(bmax >> 7);
+  const int e = (int)((bmax + (uint32_t)(127 - thr7)) >> 7);
   if (bmax == 0) return 0u;
   return (uint32_t)min(max(e - Fmt<PELEM>::emax, 0), 254);
 }
 
-// S^T for one q-block: 8 MFMAs over the 128-key tile with accumulator init C
-template <int QK, int PELEM, int D>
-__device__ __forceinline__ void scores_block(v4f (&s)[8], const uint8_t* ldsK, const uint8_t* ldsKs, const v8i& qB,
-                                             int qS, float C, int lane) {
-  constexpr int RB = D * Fmt<QK>::bits / 8;
-  const int m = lane & 15, g = lane >> 4;
+__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
+
+// Stage 1 + pack: BF16 patterns of a lane's 32 scores (element e = 16 kg + k);
+// v_cvt_u32_f32 truncates toward zero (= floor for t >= 0) and gives 0 below 0
+__device__ __forceinline__ void pack_b(const v16f (&S)[2], uint32_t (&w)[16]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int key = key_of<PELEM>(j, m & 3, m >> 2);
-    v8i a = load_row_operand<QK, D>(ldsK + key * RB, g);
-    const int sa = (D == 128 || g < 2) ? (int)ldsKs[key * 4 + g] : 127;
-    const v4f c = {C, C, C, C};
-    s[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qB, c, QK, QK, 0, sa, 0, qS);
+  for (int i = 0; i < 16; ++i) {
+    const int kg = i >> 3, k = 2 * (i & 7);
+    w[i] = __builtin_amdgcn_perm(__float2uint_rz(S[kg][k + 1]), __float2uint_rz(S[kg][k]), 0x05040100u);
   }
 }
 
-// rescale O rows (queries 4g + r of this q-block) by rho of their query (held by lane q)
-template <int D>
-__device__ __forceinline__ void rescale(v4f (&O)[D / 16], v4f& L, float rho, int lane) {
-  const int g = lane >> 4;
-  float rr[4];
+__device__ __forceinline__ float max16(const v16f& s) {
+  float m = max3f(s[0], s[1], s[2]);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) rr[r] = wshfl(rho, 4 * g + r);
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) O[i][r] *= rr[r];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) L[r] *= rr[r];
+  for (int k = 3; k < 15; k += 2) m = max3f(m, s[k], s[k + 1]);
+  return __builtin_fmaxf(m, s[15]);
 }
+__device__ __forceinline__ float max32(const v16f (&S)[2]) { return __builtin_fmaxf(max16(S[0]), max16(S[1])); }
 
-template <int PELEM>
-__device__ __forceinline__ v8i mask_half(const v8i& pA, int g, int keep_half) {
-  v8i r = pA;
-  if constexpr (Layout<PELEM>::split) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (keep_half != 0) r[i] = 0;
-      if (keep_half != 1) r[4 + i] = 0;
-    }
-  } else {
-    if ((g >> 1) != keep_half) r = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-  return r;
-}
-
-// Build the P operand (A of PV) from a lane's 32 folded scores (stage 1 + 2).
-// The caller has made every score either a normal input to stage 1 or -inf.
-template <int PELEM>
-__device__ __forceinline__ void make_p(const v4f (&s)[8], int g, int lane, bool fitmax, v8i& pA, int& pS,
-                                       uint32_t (&dsc)[2]) {
-  uint32_t w[16];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t b0 = __float2uint_rz(s[j][0]), b1 = __float2uint_rz(s[j][1]);
-    const uint32_t b2 = __float2uint_rz(s[j][2]), b3 = __float2uint_rz(s[j][3]);
-    w[2 * j] = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
-    w[2 * j + 1] = __builtin_amdgcn_perm(b3, b2, 0x05040100u);
-  }
-  if constexpr (!Layout<PELEM>::split) {
-    float tm = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int r = (j == 0 ? 3 : 0); r < 4; r += 2) tm = fmaxf(fmaxf(tm, s[j][r]), (r + 1 < 4) ? s[j][r + 1] : s[j][r]);
+// P operand from packed patterns and the lane's maxima over key groups 0/1.
+// FP6 P: the lane's 32 keys are one block.  FP8 P: elements 0-15 belong to
+// block 0 of the step, 16-31 to block 1, each block spanning lanes q and q+32.
+template <int PE>
+__device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, float m1, int lane, v8i& pA, int& pS,
+                                         uint32_t (&dsc)[2]) {
+  if constexpr (!Opd<PE>::split) {
+    const float tm = __builtin_fmaxf(m0, m1);
     const uint32_t bmax = (tm >= 128.0f) ? min(__float2uint_rz(tm), 0x7F7Fu) : 0u;
-    const uint32_t sc = p_scale<PELEM>(bmax, fitmax);
+    const uint32_t sc = p_scale<PE>(bmax);
     v16u wv;
 #pragma unroll
     for (int i = 0; i < 16; ++i) wv[i] = w[i];
     const v32bf x = __builtin_bit_cast(v32bf, wv);
     v6i r;
-    if constexpr (PELEM == E2M3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(x, e8m0_to_float(sc));
+    if constexpr (PE == E2M3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(x, e8m0_to_float(sc));
     else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(x, e8m0_to_float(sc));
     pA = v8i{r[0], r[1], r[2], r[3], r[4], r[5], 0, 0};
     pS = (int)sc;
     dsc[0] = sc;
     dsc[1] = sc;
   } else {
-    float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) { m0 = fmaxf(m0, s[j][r]); m1 = fmaxf(m1, s[4 + j][r]); }
-    m0 = fmaxf(m0, wshfl(m0, lane ^ 16));
-    m1 = fmaxf(m1, wshfl(m1, lane ^ 16));
-    const uint32_t b0 = (m0 >= 128.0f) ? min(__float2uint_rz(m0), 0x7F7Fu) : 0u;
-    const uint32_t b1 = (m1 >= 128.0f) ? min(__float2uint_rz(m1), 0x7F7Fu) : 0u;
-    const uint32_t s0 = p_scale<PELEM>(b0, fitmax), s1 = p_scale<PELEM>(b1, fitmax);
+    const float b0m = __builtin_fmaxf(m0, wshfl(m0, lane ^ 32));
+    const float b1m = __builtin_fmaxf(m1, wshfl(m1, lane ^ 32));
+    const uint32_t b0 = (b0m >= 128.0f) ? min(__float2uint_rz(b0m), 0x7F7Fu) : 0u;
+    const uint32_t b1 = (b1m >= 128.0f) ? min(__float2uint_rz(b1m), 0x7F7Fu) : 0u;
+    const uint32_t s0 = p_scale<PE>(b0), s1 = p_scale<PE>(b1);
     const float X0 = e8m0_to_float(s0), X1 = e8m0_to_float(s1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float Xi = (i < 4) ? X0 : X1;
       v2s r = {0, 0};
-      const v2bf p0 = __builtin_bit_cast(v2bf, w[2 * i]);
-      const v2bf p1 = __builtin_bit_cast(v2bf, w[2 * i + 1]);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, p0, Xi, false);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, p1, Xi, true);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf, w[2 * i]), Xi, false);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf, w[2 * i + 1]), Xi, true);
       pA[i] = (int)((uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16));
     }
-    // MFMA scale of 32-block b comes from lane 16b + n:
-    // b0 = first half of g=0,1 ; b1 = first half of g=2,3 ; b2 = second half of g=0,1 ; b3 = second half of g=2,3
-    const int n = lane & 15;
-    const int from_g2 = wshfl((int)s0, n + 32);
-    const int from_g1 = wshfl((int)s1, n + 16);
-    pS = (g == 0) ? (int)s0 : (g == 1) ? from_g2 : (g == 2) ? from_g1 : (int)s1;
+    pS = (lane >> 5) ? (int)s1 : (int)s0;  // block b's scale comes from lane 32b + q
     dsc[0] = s0;
     dsc[1] = s1;
   }
 }
 
-template <int PELEM, int VELEM, int D, int NQ>
-__device__ __forceinline__ void pv_all(v4f (&O)[NQ][D / 16], v4f (&L)[NQ], const v8i (&pA)[NQ], const int (&pS)[NQ],
-                                       const uint8_t* ldsV, const uint8_t* ldsVs, int lane) {
-  constexpr int RB = VRowLds<VELEM>::bytes;
-  const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    const int d = 16 * i + n;
-    const v8i b = load_v_operand<VELEM>(ldsV + d * RB, g);
-    const int sb = (int)ldsVs[d * 4 + g];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      O[q][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pA[q], b, O[q][i], PELEM, VELEM, 0, pS[q], 0, sb);
-  }
-  // l += P 1: ones operand (E2M1 code 0x2 = 1.0, scale 2^0)
-  const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
-#pragma unroll
-  for (int q = 0; q < NQ; ++q)
-    L[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pA[q], ones, L[q], PELEM, E2M1, 0, pS[q], 0, 127);
-}
-
 // optional P dump (debug): one code byte per key and the E8M0 per 32 keys
-template <int PELEM>
-__device__ __forceinline__ void dump_p(const FwdArgs& a, int bh, int qq, int k0, int g, const v8i& pA,
+template <int PE>
+__device__ __forceinline__ void dump_p(const FwdArgs& a, int bh, int qq, int k0, int hh, const v8i& pA,
                                        const uint32_t (&dsc)[2]) {
   if (bh != a.pd_bh || qq < a.pd_row0 || qq >= a.pd_row1 || qq >= a.Sq) return;
   const int nb32 = a.nb32;
   const size_t S32 = (size_t)nb32 * 32;
   uint8_t* drow = a.pd_codes + (size_t)(qq - a.pd_row0) * S32;
   uint8_t* srow = a.pd_scales + (size_t)(qq - a.pd_row0) * nb32;
-  constexpr int bits = Fmt<PELEM>::bits;
+  constexpr int bits = Fmt<PE>::bits;
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
-    const int key = k0 + key_of<PELEM>(e >> 2, e & 3, g);
+    const int key = k0 + step_key<PE>(e >> 4, e & 15, hh);
     const int pos = e * bits;
     uint32_t wv = (uint32_t)pA[pos >> 5] >> (pos & 31);
     if ((pos & 31) + bits > 32) wv |= (uint32_t)pA[(pos >> 5) + 1] << (32 - (pos & 31));
     if (key < (int)S32) drow[key] = (uint8_t)(wv & ((1u << bits) - 1));
   }
-  if constexpr (Layout<PELEM>::split) {
-    const int kb0 = (k0 + 16 * g) / 32, kb1 = (k0 + 64 + 16 * g) / 32;
-    if (kb0 < nb32) srow[kb0] = (uint8_t)dsc[0];
-    if (kb1 < nb32) srow[kb1] = (uint8_t)dsc[1];
+  const int kb = k0 / 32 + hh;
+  if (kb < nb32) srow[kb] = (uint8_t)(Opd<PE>::split ? dsc[hh] : dsc[0]);
+}
+
+// l accumulator: FP6 P -> 16x16 layout (v4f), FP8 P -> the layout of O (v16f)
+template <int PE> struct LAcc { typedef v4f T; };
+template <> struct LAcc<E4M3> { typedef v16f T; };
+
+// rho of query q is held by lanes q and q+32; O lane (c, h) reg 4i+j holds query 8i+4h+j
+template <int PE, int NV>
+__device__ __forceinline__ void rescale(v16f (&O)[NV], typename LAcc<PE>::T& L, float rho, int lane) {
+  const int h = lane >> 5;
+  float r[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[4 * i + j] = wshfl(rho, 8 * i + 4 * h + j);
+#pragma unroll
+  for (int o = 0; o < NV; ++o)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) O[o][k] *= r[k];
+  if constexpr (Opd<PE>::split) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) L[k] *= r[k];
   } else {
-    const int kb = (k0 + 32 * g) / 32;
-    if (kb < nb32) srow[kb] = (uint8_t)dsc[0];
+    // 16x16 layout: lane (c16, g) reg k holds l of query 4g+k (c16 < 8) or 16+4g+k
+    const int c16 = lane & 15, g = (lane >> 4) & 3;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) L[k] *= wshfl(rho, (c16 < 8 ? 0 : 16) + 4 * g + k);
   }
 }
 
-template <int PELEM, int VELEM, int D>
-__device__ __forceinline__ void pv_one(v4f (&O)[D / 16], v4f& L, const v8i& pA, int pS, const uint8_t* ldsV,
-                                       const uint8_t* ldsVs, int lane) {
-  constexpr int RB = VRowLds<VELEM>::bytes;
-  const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    const int d = 16 * i + n;
-    const v8i b = load_v_operand<VELEM>(ldsV + d * RB, g);
-    const int sb = (int)ldsVs[d * 4 + g];
-    O[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pA, b, O[i], PELEM, VELEM, 0, pS, 0, sb);
-  }
-  const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
-  L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pA, ones, L, PELEM, E2M1, 0, pS, 0, 127);
-}
-
-// The exact path for one q-block of a tile: tile-0 reference, rollback gate
-// per 64- or 128-key gate tile (the second 64-key half is re-scored with the
-// updated accumulator offset), stage-1 flush and clamp, P, and P V with the
-// mid-tile rescale when the second half fires.
-template <int QK, int VELEM, int PELEM, int D, bool DUMP>
-__device__ __forceinline__ void rare_block(v4f (&S)[8], float& C, int& cnt, v4f (&O)[D / 16], v4f& L, const v8i& qB,
-                                        int qS, int t, int nk, int k0, float T0, float Tg, const FwdArgs& a,
-                                        const uint8_t* ldsK, const uint8_t* ldsKs, const uint8_t* ldsV,
-                                        const uint8_t* ldsVs, int bh, int qbase, int lane) {
-  const int g = lane >> 4, n = lane & 15;
-  float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (half_of<PELEM>(j, g) == 0) m0 = fmaxf(m0, S[j][r]);
-      else m1 = fmaxf(m1, S[j][r]);
-    }
-  m0 = fmaxf(m0, wshfl(m0, lane ^ 16)); m0 = fmaxf(m0, wshfl(m0, lane ^ 32));
-  m1 = fmaxf(m1, wshfl(m1, lane ^ 16)); m1 = fmaxf(m1, wshfl(m1, lane ^ 32));
-  bool split = false;
-  float rho_split = 1.0f;
-  if (a.kv128) {
-    const float mx = fmaxf(m0, m1);
-    if (t == 0) {
-      C = T0 - mx;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[j][r] = S[j][r] + C;
-    } else {
-      float rho = 1.0f;
-      if (mx > Tg) {
-        const float delta = mx - T0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) S[j][r] = S[j][r] - delta;
-        C -= delta;
-        cnt += 1;
-        rho = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
-      }
-      if (__ballot(mx > Tg) != 0) rescale<D>(O, L, rho, lane);
-    }
-  } else {
-    bool recompute = false;
-    float rho0 = 1.0f;
-    if (t == 0) {
-      C = T0 - m0;  // half 0 is the reference tile (scores computed with C = 0)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (half_of<PELEM>(j, g) == 0) S[j][r] = S[j][r] + C;
-      recompute = true;
-    } else if (m0 > Tg) {
-      const float delta = m0 - T0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (half_of<PELEM>(j, g) == 0) S[j][r] = S[j][r] - delta;
-      C -= delta;
-      cnt += 1;
-      rho0 = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
-    }
-    if (t != 0 && __ballot(m0 > Tg) != 0) {
-      recompute = true;
-      rescale<D>(O, L, rho0, lane);
-    }
-    if (recompute) {
-      // half 1 is the next gate tile: re-score it with the updated C, one
-      // MFMA at a time, keeping the half-0 values of every lane
-      constexpr int RB = D * Fmt<QK>::bits / 8;
-      const int m = lane & 15;
-      const v4f ci = {C, C, C, C};
-      m1 = -INFINITY;
-#pragma unroll
-      for (int j = (Layout<PELEM>::split ? 4 : 0); j < 8; ++j) {
-        const int key = key_of<PELEM>(j, m & 3, m >> 2);
-        const v8i ka = load_row_operand<QK, D>(ldsK + key * RB, g);
-        const int sa = (D == 128 || g < 2) ? (int)ldsKs[key * 4 + g] : 127;
-        const v4f s2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qB, ci, QK, QK, 0, sa, 0, qS);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (half_of<PELEM>(j, g) == 1) {
-            const float v = (key_of<PELEM>(j, r, g) < nk) ? s2[r] : -INFINITY;
-            S[j][r] = v;
-            m1 = fmaxf(m1, v);
-          }
-      }
-      m1 = fmaxf(m1, wshfl(m1, lane ^ 16));
-      m1 = fmaxf(m1, wshfl(m1, lane ^ 32));
-    }
-    if (m1 > Tg) {
-      const float delta = m1 - T0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (half_of<PELEM>(j, g) == 1) S[j][r] = S[j][r] - delta;
-      C -= delta;
-      cnt += 1;
-      rho_split = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
-    }
-    split = __ballot(m1 > Tg) != 0;
-  }
-  // stage-1 flush (patterns with exponent field 0) and clamp, made explicit
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = S[j][r];
-      S[j][r] = (v >= 128.0f) ? fminf(v, 32639.5f) : -INFINITY;
-    }
-  v8i pA;
-  int pS;
-  uint32_t dsc[2];
-  make_p<PELEM>(S, g, lane, a.fitmax != 0, pA, pS, dsc);
-  if constexpr (DUMP) dump_p<PELEM>(a, bh, qbase + n, k0, g, pA, dsc);
-  if (!split) {
-    pv_one<PELEM, VELEM, D>(O, L, pA, pS, ldsV, ldsVs, lane);
-  } else {
-    pv_one<PELEM, VELEM, D>(O, L, mask_half<PELEM>(pA, g, 0), pS, ldsV, ldsVs, lane);
-    rescale<D>(O, L, rho_split, lane);
-    pv_one<PELEM, VELEM, D>(O, L, mask_half<PELEM>(pA, g, 1), pS, ldsV, ldsVs, lane);
-  }
-}
-
-template <int QK, int VELEM, int PELEM, int D, int NQ, bool DUMP>
+template <int QK, int VE, int PE, int D, bool KV128, bool DUMP>
 __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
-  constexpr int QRB = D * Fmt<QK>::bits / 8;      // Q/K row bytes
-  constexpr int VBB = Fmt<VELEM>::bits * 4;       // V block bytes
-  constexpr int VRB = VRowLds<VELEM>::bytes;      // V LDS row bytes (one d row, 128 keys)
-  constexpr int SZ_K = KT * QRB, SZ_KS = KT * 4, SZ_V = D * VRB, SZ_VS = D * 4;
-  constexpr int STAGE = SZ_K + SZ_KS + SZ_V + SZ_VS;
-  constexpr int QWG = NW * NQ * 16;  // queries per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  using G = Geo<QK, VE, D>;
+  using LT = typename LAcc<PE>::T;
+  constexpr int NV = G::NV;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * G::SLOT];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
   const int bh = blockIdx.y + blockIdx.z * a.H;
   const int Sq = a.Sq, Skv = a.Skv, nb32 = a.nb32;
-  const int qw0 = blockIdx.x * QWG + w * NQ * 16;  // first query of this wave
+  const int qw0 = blockIdx.x * QWG + w * QW;
+  const int ns = (Skv + KS - 1) / KS;
 
-  const uint8_t* kbase = a.kc + (size_t)bh * Skv * QRB;
-  const uint8_t* ksbase = a.ks + (size_t)bh * Skv * (D / 32);
-  const uint8_t* vbase = a.vc + (size_t)bh * D * nb32 * VBB;
-  const uint8_t* vsbase = a.vs + (size_t)bh * D * nb32;
+  DmaSrc<QK, VE, PE, D> src;
+  src.k = a.kc + (size_t)bh * Skv * G::QRB;
+  // K scales are read a dword at a time; for D = 64 (two bytes per key) the
+  // head may start in the middle of a dword: read from the dword boundary and
+  // shift every key by one
+  const size_t ks0 = (size_t)bh * Skv * G::KSB;
+  src.ko = (D == 64) ? (int)((ks0 >> 1) & 1) : 0;
+  src.ks = a.ks + (ks0 & ~(size_t)3);
+  src.v = a.vc + (size_t)bh * D * nb32 * G::VBB;
+  src.vs = a.vs + (size_t)bh * nb32 * 128;
+  src.kb = (int64_t)Skv * G::QRB;
+  src.ksb = ((int64_t)(Skv + src.ko) * G::KSB + 3) & ~(int64_t)3;
+  src.vb = (int64_t)D * nb32 * G::VBB;
+  src.vsb = (int64_t)nb32 * 128;
 
-  // ---- per q-block state
-  v8i qB[NQ];
-  int qS[NQ];
-  float C[NQ];
-  int cnt[NQ];
-  v4f O[NQ][D / 16];
-  v4f L[NQ];
+  // ---- this wave's DMA items (the same every step)
+  Dma d16[G::M16], d4[G::M4];
+  int n16 = 0, n4 = 0;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int qrow = min(qw0 + 16 * q + n, Sq - 1);
-    const uint8_t* qp = a.qc + ((size_t)bh * Sq + qrow) * QRB;
-    qB[q] = load_row_operand<QK, D>(qp, g);
-    qS[q] = (D == 128 || g < 2) ? (int)a.qs[((size_t)bh * Sq + qrow) * (D / 32) + g] : 127;
-    C[q] = 0.0f;
-    cnt[q] = 0;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) O[q][i] = v4f{0.f, 0.f, 0.f, 0.f};
-    L[q] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  const float T0 = a.T0, Tg = a.Tg;
-  const float TgEff = fminf(Tg, 32639.0f);  // above this the stage-1 clamp could act: take the exact path
-  const bool fitmax = a.fitmax != 0;
-  const int ntiles = (Skv + KT - 1) / KT;
-
-  // ---- tile loaders: codes by direct global->LDS DMA, scales through registers
-  [[maybe_unused]] auto issue_codes = [&](int t, int s) {
-    uint8_t* base = smem + s * STAGE;
-    const int k0 = t * KT;
-    {
-      const int64_t lim = (int64_t)Skv * QRB - 16;
-#pragma unroll
-      for (int i = w; i < SZ_K / 1024; i += NW) {
-        int64_t off = (int64_t)k0 * QRB + i * 1024 + lane * 16;
-        off = off < lim ? off : lim;
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (void*)(base + i * 1024), 16, 0, 0);
-      }
-    }
-    {
-      // every lane moves one chunk to LDS offset 16*(64*i + lane) of the V
-      // region: 16 bytes of a 16/32-byte block, or one 12-byte half of a
-      // 24-byte FP6 block (padded slot)
-      constexpr int CPB = VRowLds<VELEM>::block / 16;  // LDS chunks per block
-#pragma unroll
-      for (int i = w; i < SZ_V / 1024; i += NW) {
-        const int ci = i * 64 + lane;
-        const int d = ci / (4 * CPB), rem = ci - d * 4 * CPB;
-        const int blk = min(4 * t + rem / CPB, nb32 - 1);
-        const int part = rem % CPB;
-        const uint8_t* gp = vbase + ((size_t)d * nb32 + blk) * VBB + part * (VBB == 24 ? 12 : 16);
-        if constexpr (VBB == 24) __builtin_amdgcn_global_load_lds((const void*)gp, (void*)(base + SZ_K + SZ_KS + i * 1024), 12, 0, 0);
-        else __builtin_amdgcn_global_load_lds((const void*)gp, (void*)(base + SZ_K + SZ_KS + i * 1024), 16, 0, 0);
-      }
-    }
-  };
-  // register-staged copy of the K/V codes of tile t (used when direct loads are off)
-  constexpr int NK4 = SZ_K / (NW * 64 * 16), NVW = D * VBB / (NW * 64);  // V words per thread (D*4 blocks)
-  uint4 kst[NK4 > 0 ? NK4 : 1];
-  uint32_t vst[NVW > 0 ? NVW : 1];
-  [[maybe_unused]] auto load_codes_regs = [&](int t) {
-    const int k0 = t * KT;
-    const int64_t lim = (int64_t)Skv * QRB - 16;
-#pragma unroll
-    for (int i = 0; i < NK4; ++i) {
-      int64_t off = (int64_t)k0 * QRB + (int64_t)(i * NW * 64 + tid) * 16;
-      off = off < lim ? off : lim;
-      kst[i] = *reinterpret_cast<const uint4*>(kbase + off);
-    }
-#pragma unroll
-    for (int i = 0; i < NVW; ++i) {
-      const int wi = i * NW * 64 + tid;  // word index over [d][4 blocks][VBB/4 words]
-      const int d = wi / (VBB), rem = wi - d * VBB;
-      const int blk = min(4 * t + rem / (VBB / 4), nb32 - 1);
-      const int wd = rem % (VBB / 4);
-      vst[i] = *reinterpret_cast<const uint32_t*>(vbase + ((size_t)d * nb32 + blk) * VBB + 4 * wd);
-    }
-  };
-  [[maybe_unused]] auto store_codes_regs = [&](int s) {
-    uint8_t* base = smem + s * STAGE;
-#pragma unroll
-    for (int i = 0; i < NK4; ++i) *reinterpret_cast<uint4*>(base + (i * NW * 64 + tid) * 16) = kst[i];
-#pragma unroll
-    for (int i = 0; i < NVW; ++i) {
-      const int wi = i * NW * 64 + tid;
-      const int d = wi / (VBB), rem = wi - d * VBB;
-      const int blk = rem / (VBB / 4), byte = 4 * (rem % (VBB / 4));
-      const int slot = (VBB == 24 && byte >= 12) ? byte + 4 : byte;
-      *reinterpret_cast<uint32_t*>(base + SZ_K + SZ_KS + d * VRB + blk * VRowLds<VELEM>::block + slot) = vst[i];
-    }
-  };
-  auto load_scales = [&](int t) -> uint32_t {
-    uint32_t r = 0;
-    if (tid < KT) {
-      const int key = min(t * KT + tid, Skv - 1);
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) r |= (uint32_t)ksbase[(size_t)key * (D / 32) + e] << (8 * e);
-    } else if (tid < KT + D) {
-      const int d = tid - KT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int blk = min(4 * t + e, nb32 - 1);
-        r |= (uint32_t)vsbase[(size_t)d * nb32 + blk] << (8 * e);
-      }
-    }
-    return r;
-  };
-  auto store_scales = [&](uint32_t r, int s) {
-    uint8_t* base = smem + s * STAGE;
-    if (tid < KT) *reinterpret_cast<uint32_t*>(base + SZ_K + 4 * tid) = r;
-    else if (tid < KT + D) *reinterpret_cast<uint32_t*>(base + SZ_K + SZ_KS + SZ_V + 4 * (tid - KT)) = r;
-  };
-
-#if FSATTN_LDS_DIRECT
-  issue_codes(0, 0);
-#else
-  load_codes_regs(0);
-  store_codes_regs(0);
-#endif
-  store_scales(load_scales(0), 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const bool more = t + 1 < ntiles;
-    uint32_t sreg = 0;
-    if (more) {
-#if FSATTN_LDS_DIRECT
-      issue_codes(t + 1, cur ^ 1);
-#else
-      load_codes_regs(t + 1);
-#endif
-      sreg = load_scales(t + 1);
-    }
-    const uint8_t* ldsK = smem + cur * STAGE;
-    const uint8_t* ldsKs = ldsK + SZ_K;
-    const uint8_t* ldsV = ldsKs + SZ_KS;
-    const uint8_t* ldsVs = ldsV + SZ_V;
-    const int k0 = t * KT;
-    const int nk = min(KT, Skv - k0);
-
-    // ---- folded scores S^T = C + K Q^T for every q-block (K operand shared)
-    v4f S[NQ][8];
-    {
-      constexpr int RB = QRB;
-      const int m = lane & 15;
-      v4f cinit[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) cinit[q] = v4f{C[q], C[q], C[q], C[q]};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = key_of<PELEM>(j, m & 3, m >> 2);
-        const v8i ka = load_row_operand<QK, D>(ldsK + key * RB, g);
-        const int sa = (D == 128 || g < 2) ? (int)ldsKs[key * 4 + g] : 127;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          S[q][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qB[q], cinit[q], QK, QK, 0, sa, 0, qS[q]);
-      }
-    }
-    if (nk < KT) {  // keys beyond Skv: -inf (stage 1 -> 0, excluded from maxima)
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (key_of<PELEM>(j, r, g) >= nk) S[q][j][r] = -INFINITY;
-    }
-
-    // ---- fast-path check on the block maxima
-    bool rare = (t == 0);
-    if (!rare) {
-      bool flag = false;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        float tm = -INFINITY, lo = INFINITY;
-        if constexpr (!Layout<PELEM>::split) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) tm = fmaxf(fmaxf(tm, fmaxf(S[q][j][0], S[q][j][1])), fmaxf(S[q][j][2], S[q][j][3]));
-          lo = tm;
-        } else {
-          float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            m0 = fmaxf(fmaxf(m0, fmaxf(S[q][j][0], S[q][j][1])), fmaxf(S[q][j][2], S[q][j][3]));
-            m1 = fmaxf(fmaxf(m1, fmaxf(S[q][4 + j][0], S[q][4 + j][1])), fmaxf(S[q][4 + j][2], S[q][4 + j][3]));
-          }
-          m0 = fmaxf(m0, wshfl(m0, lane ^ 16));
-          m1 = fmaxf(m1, wshfl(m1, lane ^ 16));
-          tm = fmaxf(m0, m1);
-          lo = fminf(m0, m1);
-        }
-        flag |= (tm > TgEff) || (lo < PFlush<PELEM>::t);
-      }
-      rare = __ballot(flag) != 0;
-    }
-
-    if (rare) {
-      // exact per-row gate semantics, BF16 flush and clamp; one q-block at a time
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        rare_block<QK, VELEM, PELEM, D, DUMP>(S[q], C[q], cnt[q], O[q], L[q], qB[q], qS[q], t, nk, k0, T0, Tg, a,
-                                              ldsK, ldsKs, ldsV, ldsVs, bh, qw0 + 16 * q, lane);
+  for (int k = 0; k < G::M16; ++k) {
+    const int it = w + NW * k;
+    if (it < G::N16) {
+      d16[k] = dma16<QK, VE, PE, D>(it, lane, nb32, src);
+      ++n16;
     } else {
-      // ---- stage 1 + 2 -> P operands, then O += P V ; l += P 1 (same P)
-      v8i pA[NQ];
-      int pS[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        uint32_t dsc[2];
-        make_p<PELEM>(S[q], g, lane, fitmax, pA[q], pS[q], dsc);
-        if constexpr (DUMP) dump_p<PELEM>(a, bh, qw0 + 16 * q + n, k0, g, pA[q], dsc);
-      }
-      pv_all<PELEM, VELEM, D, NQ>(O, L, pA, pS, ldsV, ldsVs, lane);
+      d16[k] = Dma{src.k, 0, 0, 0, 0};
     }
-
-    if (more) {
-      store_scales(sreg, cur ^ 1);
-#if !FSATTN_LDS_DIRECT
-      store_codes_regs(cur ^ 1);
-#endif
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
+#pragma unroll
+  for (int k = 0; k < G::M4; ++k) {
+    const int it = w + NW * k;
+    if (it < G::N4) {
+      d4[k] = dma4<QK, VE, PE, D>(it, lane, nb32, src);
+      ++n4;
+    } else {
+      d4[k] = Dma{src.k, 0, 0, 0, 0};
+    }
+  }
+  const int nper = n16 + n4;
+
+  auto issue = [&](int s) {
+    const uint8_t* slot = smem + (s % NS) * G::SLOT;
+#pragma unroll
+    for (int k = 0; k < G::M16; ++k) {
+      if (k < n16) {
+        const int64_t off = (int64_t)s * d16[k].stride;
+        dma_x4(rsrc(d16[k].base + off, d16[k].bytes - off), lds_addr(slot + d16[k].lds), d16[k].voff);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < G::M4; ++k) {
+      if (k < n4) {
+        const int64_t off = (int64_t)s * d4[k].stride;
+        dma_x1(rsrc(d4[k].base + off, d4[k].bytes - off), lds_addr(slot + d4[k].lds), d4[k].voff);
+      }
+    }
+  };
+
+  // ---- Q operands (B of the score product) and their scales
+  v8i qB[G::DH];
+  int qS[G::DH];
+  {
+    const int qrow = min(qw0 + n, Sq - 1);
+    const uint8_t* qp = a.qc + ((size_t)bh * Sq + qrow) * G::QRB;
+    const uint8_t* qsp = a.qs + ((size_t)bh * Sq + qrow) * G::KSB;
+#pragma unroll
+    for (int dh = 0; dh < G::DH; ++dh) {
+      int ca, cb;
+      k_chunks<QK, D>(0, dh, hh, ca, cb);
+      const uint2 x0 = *reinterpret_cast<const uint2*>(qp + ca);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(qp + ca + 8);
+      v8i r = {(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y, 0, 0, 0, 0};
+      if constexpr (Opd<QK>::tail == 16) {
+        const uint4 y = *reinterpret_cast<const uint4*>(qp + cb);
+        r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+      } else if constexpr (Opd<QK>::tail == 8) {
+        const uint2 y = *reinterpret_cast<const uint2*>(qp + cb);
+        r[4] = y.x; r[5] = y.y;
+      }
+      qB[dh] = r;
+      qS[dh] = (int)qsp[2 * dh + hh];
+    }
+  }
+  // K scale shift per key group: the dword holds the key's block scales
+  // (D = 128) or those of an even/odd key pair (D = 64)
+  int ksh[2];
+#pragma unroll
+  for (int kg = 0; kg < 2; ++kg) {
+    const int key = row_key<PE>(kg, n) + src.ko;
+    ksh[kg] = (D == 128) ? 8 * hh : 16 * (key & 1) + 8 * hh;
+  }
+  // ones operand of the l product.  FP6 P (16x16x128, lanes read as rows
+  // l%16 and K blocks l/16): column c16 < 8 sums the blocks of query r
+  // (K blocks 0 and 2), c16 >= 8 those of query r+16 (blocks 1 and 3).
+  v8i ones;
+  if constexpr (Opd<PE>::split) {
+    ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  } else {
+    const int c16 = lane & 15, g = lane >> 4;
+    const bool on = ((g & 1) == 0) == (c16 < 8);
+    const int v = on ? 0x22222222 : 0;
+    ones = v8i{v, v, v, v, 0, 0, 0, 0};
+  }
+
+  const float T0 = a.T0, Tg = a.Tg;
+  const float TgEff = fminf(Tg, 32639.0f);  // above this the stage-1 clamp could act: exact path
+
+  float C = 0.0f;
+  v16f Cv;  // C splat: the accumulator's initial value of the score product
+#pragma unroll
+  for (int k = 0; k < 16; ++k) Cv[k] = 0.0f;
+  auto set_C = [&](float c) {
+    C = c;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) Cv[k] = c;
+  };
+  int cnt = 0;
+  v16f O[NV];
+#pragma unroll
+  for (int o = 0; o < NV; ++o)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) O[o][k] = 0.0f;
+  LT L;
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(LT) / 4); ++k) L[k] = 0.0f;
+
+  auto scores = [&](v16f (&S)[2], int s) {
+    const uint8_t* slot = smem + (s % NS) * G::SLOT;
+    const uint32_t kd0 = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 4 * n) >> ksh[0];
+    const uint32_t kd1 = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 128 + 4 * n) >> ksh[1];
+    // both key groups' first feature half (initial value C), then the second
+#pragma unroll
+    for (int dh = 0; dh < G::DH; ++dh)
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
+        const int ksc = (int)(kg ? kd1 : kd0);
+        const v8i ka = lds_operand<QK>(slot + G::K_OFF + (kg * G::DH + dh) * Opd<QK>::region, lane);
+        if (dh == 0)
+          S[kg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qB[0], Cv, QK, QK, 0, ksc, 0, qS[0]);
+        else
+          S[kg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qB[G::DH - 1], S[kg], QK, QK, 2, ksc, 0,
+                                                                  qS[G::DH - 1]);
+      }
+  };
+  auto pv = [&](const v8i& pA, int pS, int s) {
+    const uint8_t* slot = smem + (s % NS) * G::SLOT;
+    const int vsc = *reinterpret_cast<const int*>(slot + G::VS_OFF + 4 * lane);
+#pragma unroll
+    for (int o = 0; o < NV; ++o) {
+      const v8i vb = lds_operand<VE>(slot + G::V_OFF + o * Opd<VE>::region, lane);
+      if (o == 0) O[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, vb, O[0], PE, VE, 0, pS, 0, vsc);
+      if (o == 1) O[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, vb, O[1], PE, VE, 0, pS, 1, vsc);
+      if constexpr (NV > 2) {
+        if (o == 2) O[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, vb, O[2], PE, VE, 0, pS, 2, vsc);
+        if (o == 3) O[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, vb, O[3], PE, VE, 0, pS, 3, vsc);
+      }
+    }
+    if constexpr (Opd<PE>::split)
+      L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, ones, L, PE, E4M3, 0, pS, 0, 127);
+    else
+      L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pA, ones, L, PE, E2M1, 0, pS, 0, 127);
+  };
+  auto mask = [&](v16f (&S)[2], int nk) {
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (step_key<PE>(kg, k, hh) >= nk) S[kg][k] = -INFINITY;
+  };
+  auto shift = [&](v16f (&S)[2], float d) {
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) S[kg][k] = S[kg][k] + d;
+  };
+
+  // ---- prologue: fetch PF steps and make steps 0 and 1 visible
+  const int npro = min(PF, ns);
+  for (int s = 0; s < npro; ++s) issue(s);
+  wait_steps(nper, npro == PF);
+  barrier();
+
+  v16f S[2];
+  [[maybe_unused]] v16f Sn[2];  // kv_tile 128: scores of the second half of the gate tile
+  v8i pA = {0, 0, 0, 0, 0, 0, 0, 0};
+  int pS = 127;
+
+  for (int u = 0; u < ns; ++u) {
+    if (u > 0) {
+      wait_steps(nper, ns - 2 - u >= PF - 2);
+      barrier();
+    }
+    if (u + PF < ns) issue(u + PF);
+    const bool even = (u & 1) == 0;
+    const bool has_next = u + 1 < ns;
+    if constexpr (KV128) {
+      if (even) {
+        scores(S, u);
+        if (has_next) scores(Sn, u + 1);
+      } else {
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg) S[kg] = Sn[kg];
+      }
+    } else {
+      scores(S, u);
+    }
+    if (u > 0) pv(pA, pS, u - 1);
+
+    // ---- stage 1 + 2 on step u
+    const int k0 = u * KS;
+    const int nk = min(KS, Skv - k0);
+    uint32_t wv[16];
+    pack_b(S, wv);
+    const float m0 = max16(S[0]), m1 = max16(S[1]);
+    float tm, lo;
+    if constexpr (Opd<PE>::split) {
+      const float b0 = __builtin_fmaxf(m0, wshfl(m0, lane ^ 32)), b1 = __builtin_fmaxf(m1, wshfl(m1, lane ^ 32));
+      lo = __builtin_fminf(b0, b1);
+      tm = __builtin_fmaxf(b0, b1);
+    } else {
+      tm = __builtin_fmaxf(m0, m1);
+      lo = tm;
+    }
+    if constexpr (KV128) {
+      if (even && has_next) tm = __builtin_fmaxf(tm, max32(Sn));
+    }
+    const bool bad = !(tm <= TgEff) || !(lo >= PFlush<PE>::t);
+    const bool rare = (u == 0) || (nk < KS) || (__ballot(bad) != 0);
+    uint32_t dsc[2];
+    if (!rare) {
+      p_from_w<PE>(wv, m0, m1, lane, pA, pS, dsc);
+    } else {
+      // ---- exact path: masking, reference, gate, flush and clamp
+      mask(S, nk);
+      float m = max32(S);
+      m = __builtin_fmaxf(m, wshfl(m, lane ^ 32));
+      bool pair = false;  // the gate tile spans steps u and u+1
+      if constexpr (KV128) {
+        pair = even && has_next;
+        if (pair) {
+          mask(Sn, min(KS, Skv - k0 - KS));
+          float mn = max32(Sn);
+          m = __builtin_fmaxf(m, __builtin_fmaxf(mn, wshfl(mn, lane ^ 32)));
+        }
+      }
+      float rho = 1.0f;
+      bool any_fire = false;
+      if (u == 0) {
+        set_C(T0 - m);
+        shift(S, C);
+        if constexpr (KV128) {
+          if (pair) shift(Sn, C);
+        }
+      } else if (!KV128 || even) {
+        const bool fire = m > Tg;
+        const float delta = fire ? m - T0 : 0.0f;
+        if (fire) {
+          shift(S, -delta);
+          cnt += 1;
+          rho = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
+          if constexpr (KV128) {
+            if (pair) shift(Sn, -delta);
+          }
+        }
+        any_fire = __ballot(fire) != 0;
+        if (any_fire) set_C(C - delta);
+      }
+      float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float v = S[kg][k];
+          const float f = (v >= 128.0f) ? __builtin_fminf(v, 32639.5f) : -INFINITY;
+          S[kg][k] = f;
+          if (kg == 0) mx0 = __builtin_fmaxf(mx0, f);
+          else mx1 = __builtin_fmaxf(mx1, f);
+        }
+      pack_b(S, wv);
+      p_from_w<PE>(wv, mx0, mx1, lane, pA, pS, dsc);
+      if (any_fire) rescale<PE, NV>(O, L, rho, lane);
+    }
+    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, k0, hh, pA, dsc);
+  }
+  pv(pA, pS, ns - 1);
 
   // ---- epilogue: O / l -> bf16; counts
+  float lq[16];
+  if constexpr (Opd<PE>::split) {
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
+    for (int k = 0; k < 16; ++k) lq[k] = L[k];
+  } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qq = qw0 + 16 * q + 4 * g + r;
+    for (int i = 0; i < 4; ++i) {
+      const int srcl = 16 * (2 * (i & 1) + hh) + 8 * (i >> 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lq[4 * i + j] = wshfl(L[j], srcl);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int qq = qw0 + 8 * i + 4 * hh + j;
       if (qq < Sq) {
-        const float inv = 1.0f / L[q][r];
+        const float inv = 1.0f / lq[4 * i + j];
         uint16_t* orow = a.out + ((size_t)bh * Sq + qq) * D;
 #pragma unroll
-        for (int i = 0; i < D / 16; ++i) {
-          uint32_t u = __float_as_uint(O[q][i][r] * inv);
-          u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // RNE to bf16 (finite values)
-          orow[16 * i + n] = (uint16_t)u;
+        for (int o = 0; o < NV; ++o) {
+          uint32_t uo = __float_as_uint(O[o][4 * i + j] * inv);
+          uo = (uo + 0x7FFFu + ((uo >> 16) & 1u)) >> 16;  // RNE to bf16 (finite values)
+          orow[32 * o + n] = (uint16_t)uo;
         }
       }
     }
-    if (a.counts != nullptr && g == 0 && qw0 + 16 * q + n < Sq) a.counts[(size_t)bh * Sq + qw0 + 16 * q + n] = cnt[q];
-  }
+  if (a.counts != nullptr && hh == 0 && qw0 + n < Sq) a.counts[(size_t)bh * Sq + qw0 + n] = cnt;
 }
 
 template <int QK, int VE, int PE, int D>
-static hipError_t launch_t(const FwdArgs& a, int B, hipStream_t stream) {
-  constexpr int NQ = FSATTN_NQ;
-  dim3 grid((unsigned)((a.Sq + NW * NQ * 16 - 1) / (NW * NQ * 16)), (unsigned)a.H, (unsigned)B);
-  if (a.pd_codes != nullptr)
-    hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, NQ, true>), grid, dim3(NW * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, NQ, false>), grid, dim3(NW * 64), 0, stream, a);
+hipError_t launch_t(const FwdArgs& a, int B, hipStream_t stream) {
+  dim3 grid((unsigned)((a.Sq + QWG - 1) / QWG), (unsigned)a.H, (unsigned)B);
+  const bool dump = a.pd_codes != nullptr;
+  if (a.kv128) {
+    if (dump) hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, true, true>), grid, dim3(NW * 64), 0, stream, a);
+    else hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, true, false>), grid, dim3(NW * 64), 0, stream, a);
+  } else {
+    if (dump) hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, false, true>), grid, dim3(NW * 64), 0, stream, a);
+    else hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, false, false>), grid, dim3(NW * 64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 template <int QK, int VE, int PE>
-static hipError_t launch_d(const FwdArgs& a, int B, int D, hipStream_t s) {
+hipError_t launch_d(const FwdArgs& a, int B, int D, hipStream_t s) {
   return D == 128 ? launch_t<QK, VE, PE, 128>(a, B, s) : launch_t<QK, VE, PE, 64>(a, B, s);
 }
+
+}  // namespace
 
 // supported combinations: FP8 P with FP8 V; FP6 (E2M3) P with FP6 or FP4 V
 bool fwd_supported(int qk, int ve, int pe) {

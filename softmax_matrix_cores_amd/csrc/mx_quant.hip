@@ -174,6 +174,9 @@ __global__ void __launch_bounds__(256) mxq_axis0_kernel(const uint16_t* __restri
 
 // axis 1: lane (m, key block kb, column d), d fastest so a wave's loads of one
 // key row are contiguous; output row d holds the key blocks of that column.
+// Scales are written block-major with the columns interleaved:
+// [m][kb][d % 32][d / 32] (cols <= 128), so the four scales a PV lane needs
+// for one key block sit in one dword.
 template <int ELEM>
 __global__ void __launch_bounds__(256) mxq_axis1_kernel(const uint16_t* __restrict__ src, int64_t n_mat,
                                                         int64_t rows, int64_t cols, int64_t ld, int64_t nb,
@@ -197,7 +200,7 @@ __global__ void __launch_bounds__(256) mxq_axis1_kernel(const uint16_t* __restri
   uint32_t code = quant_block<ELEM>(x, fitmax, w, prescale == 1.0f);
   int64_t o = (m * cols + d) * nb + kb;
   store_block<BB>(codes + o * BB, w);
-  scales[o] = (uint8_t)code;
+  scales[((m * nb + kb) * 32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)code;
 }
 
 template <int ELEM>

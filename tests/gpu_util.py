@@ -41,10 +41,28 @@ def gpu_quant(q, k, v, w: W.Workload):
     return fs.quantize_qkv(q.to(dev), k.to(dev), v.to(dev), w.qk_elem, w.v_elem, w.sigma)
 
 
-def same_bytes(gpu: fs.MXTensor, ora) -> tuple[bool, bool]:
+def interleave_v_scales(s: np.ndarray) -> np.ndarray:
+    """Oracle V scales [n, cols, nb] -> the library's block-major layout
+    [n, nb, 32, 4] (column c at [c % 32][c // 32]); absent columns compare as 0."""
+    n, cols, nb = s.shape
+    out = np.zeros((n, nb, 32, 4), np.uint8)
+    for c in range(cols):
+        out[:, :, c % 32, c // 32] = s[:, c, :]
+    return out
+
+
+def same_bytes(gpu: fs.MXTensor, ora, axis: int = 0) -> tuple[bool, bool]:
     gc = gpu.codes.cpu().numpy().ravel()
     gs = gpu.scales.cpu().numpy().ravel()
-    return np.array_equal(gc, ora[0].ravel()), np.array_equal(gs, ora[1].ravel())
+    if axis == 0:
+        os_ = ora[1].ravel()
+        return np.array_equal(gc, ora[0].ravel()), np.array_equal(gs[: os_.size], os_)
+    os_ = interleave_v_scales(ora[1])
+    n, cols = ora[1].shape[0], ora[1].shape[1]
+    gs4 = gs.reshape(os_.shape).copy()
+    if cols < 128:
+        gs4[:, :, :, (cols + 31) // 32:] = 0
+    return np.array_equal(gc, ora[0].ravel()), np.array_equal(gs4, os_)
 
 
 def oracle_params(O, w: W.Workload, tau=None, kv_tile=None):
@@ -94,7 +112,7 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
     if check_quant:
         res["quant_q"] = same_bytes(Qg, Qo)
         res["quant_k"] = same_bytes(Kg, Ko)
-        res["quant_v"] = same_bytes(Vg, Vo)
+        res["quant_v"] = same_bytes(Vg, Vo, axis=1)
     p = oracle_params(O, w, tau=tau_, kv_tile=kvt)
     row_ids = None if rows is None else np.asarray(rows, dtype=np.int64)
     r = O.forward(p, Qo, Ko, Vo, rows=row_ids)
