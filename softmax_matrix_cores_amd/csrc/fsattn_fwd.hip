@@ -14,26 +14,28 @@
 //     than tau: the reference is raised and O, l are rescaled.
 //
 // Mapping to CDNA4:
-//   * 8 waves per workgroup (two per SIMD), 32 queries per wave.  With two
-//     resident waves a SIMD overlaps one wave's softmax VALU work with the
-//     other's matrix instructions.
-//   * keys advance in steps of 64, one gate tile.  Every product is
-//     v_mfma_scale_f32_32x32x64_f8f6f4: S^T = K Q^T (2 key groups x D/64
-//     feature halves, the fold offset C_i as the accumulator's initial value),
-//     O += P V (D/32 feature blocks).  l += P 1 uses one 16x16x128
-//     instruction whose ones operand selects, per output column, the lanes of
-//     one query (FP6 P), or a 32x32x64 ones operand (FP8 P).
+//   * 8 waves per workgroup (two per SIMD), 32 queries per wave.  Keys advance
+//     in steps of 64 with one workgroup barrier per step.  The two waves of a
+//     SIMD run the step in opposite phase ("ping-pong"): waves 0-3 issue the
+//     score and PV products of a step and then convert the scores on the
+//     VALU; waves 4-7 first convert the previous step's scores and then issue
+//     their products.  Between two barriers one wave of each SIMD keeps the
+//     matrix core busy while the other works on the VALU.
+//   * every product is v_mfma_scale_f32_32x32x64_f8f6f4: S^T = K Q^T (2 key
+//     groups x D/64 feature halves, the fold offset C_i as the accumulator's
+//     initial value), O += P V (D/32 feature blocks).  l += P 1 uses one
+//     16x16x128 instruction whose ones operand selects, per output column, the
+//     lanes of one query (FP6 P), or a 32x32x64 ones operand (FP8 P).
 //   * the K rows of the score instructions are permuted so that a lane's 32
 //     scores are exactly the 32 keys of its P operand in the PV product.
-//   * step u issues its score product and the PV product of step u-1 on the
-//     matrix cores, then converts the scores of step u on the VALU while the
-//     PV instructions run.
 //   * K and V operands sit in an 8-slot LDS ring in operand order, so every
 //     operand read is a lane-contiguous ds_read_b128 (plus a ds_read_b64 for
-//     the last 8 bytes of an FP6 lane): no bank conflicts.  The ring is
-//     filled six steps ahead by buffer_load ... lds DMA with constant per-lane
-//     offsets; the step moves the buffer descriptor, so reads past the end of
-//     K or V return zeros.
+//     the last 8 bytes of an FP6 lane): no bank conflicts.  The ring is filled
+//     six steps ahead by buffer_load ... lds DMA.  Every wave issues the same
+//     number of loads per step (padding loads read past the end of the buffer
+//     into a sink), so each wave waits with one constant s_waitcnt; the step
+//     moves the buffer descriptors, so reads past the end of K or V return
+//     zeros.
 //   * scales: one dword per key holds its K block scales; V scales come in the
 //     quantizer's interleaved layout, one dword per lane holding the scales of
 //     its PV instructions, picked with op_sel.
@@ -43,6 +45,9 @@
 //     32 keys.  A wave ballot sends a step to the exact path on the first
 //     step, a partial last step, a possible gate fire or stage-1 clamp, or a
 //     block low enough that the BF16 subnormal flush could change a code.
+//   * a 128-key gate tile spans two steps: on the even step the scores of the
+//     odd step are computed once ahead of time for their maximum only, and
+//     computed again (with the gate's new offset) on the odd step.
 //
 // Operand lane layouts of the 32x32x64 scaled MFMA (measured on gfx950):
 //   FP6/FP4: lane (r = l%32, h = l/32) holds row r, K elements [32h, 32h+32)
@@ -52,6 +57,8 @@
 //     lane 32b + r.
 //   Accumulator: lane (c = l%32, h) register 4i+j holds row 8i+4h+j of
 //     column c.
+#include <type_traits>
+
 #include "internal.h"
 #include "mx_device.h"
 
@@ -84,12 +91,21 @@ template <int QK, int VE, int D> struct Geo {
   static constexpr int KS_OFF = NK * Opd<QK>::region;
   static constexpr int V_OFF = KS_OFF + 256;
   static constexpr int VS_OFF = V_OFF + NV * Opd<VE>::region;
-  static constexpr int SLOT = VS_OFF + 256;
-  // DMA instructions per step with 16-byte and 4-byte lanes
-  static constexpr int N16 = NK + NV + (Opd<QK>::tail == 16 ? NK : 0) + (Opd<VE>::tail == 16 ? NV : 0);
-  static constexpr int N4 = (Opd<QK>::tail == 8 ? 2 * NK : 0) + (Opd<VE>::tail == 8 ? 2 * NV : 0) + 2;
-  static constexpr int M16 = (N16 + NW - 1) / NW;
-  static constexpr int M4 = (N4 + NW - 1) / NW;
+  static constexpr int SINK_OFF = VS_OFF + 256;  // 1 KiB per slot for padding loads
+  static constexpr int SLOT = SINK_OFF + 1024;
+  static constexpr int LDS_BYTES = NS * SLOT;
+  // DMA per step: waves 0-3 fetch K, waves 4-7 V.  16-byte loads: operand
+  // heads (and FP8 tails); 4-byte loads: FP6 tails (two per operand); one
+  // 4-byte load of the scale dwords.  Every wave issues M16 + MT + 1 loads,
+  // padded with loads that read past the end of the buffer (zeros) into the
+  // slot's sink.
+  static constexpr int N16K = NK * (Opd<QK>::tail == 16 ? 2 : 1);
+  static constexpr int NTK = Opd<QK>::tail == 8 ? 2 * NK : 0;
+  static constexpr int N16V = NV * (Opd<VE>::tail == 16 ? 2 : 1);
+  static constexpr int NTV = Opd<VE>::tail == 8 ? 2 * NV : 0;
+  static constexpr int M16 = ((N16K > N16V ? N16K : N16V) + 3) / 4;
+  static constexpr int MT = ((NTK > NTV ? NTK : NTV) + 3) / 4;
+  static constexpr int PER_WAVE = M16 + MT + 1;
 };
 
 // key (0..63 in the step) of accumulator register k (0..15) of key group kg, lane half h
@@ -115,54 +131,39 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   // s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// Wait until this wave's DMA of the oldest needed step has landed: with a
-// full pipeline PF-2 younger steps (n loads each) may still be in flight,
-// otherwise wait for everything.
-__device__ __forceinline__ void wait_steps(int n, bool full) {
-  if (!full) { wait_vm<0>(); return; }
-  switch (n) {
-    case 0: break;
-    case 1: wait_vm<(PF - 2) * 1>(); break;
-    case 2: wait_vm<(PF - 2) * 2>(); break;
-    case 3: wait_vm<(PF - 2) * 3>(); break;
-    case 4: wait_vm<(PF - 2) * 4>(); break;
-    case 5: wait_vm<(PF - 2) * 5>(); break;
-    default: wait_vm<0>(); break;
-  }
-}
-
 // workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every outstanding DMA); the clobber keeps LDS reads below it
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Buffer descriptor (raw, stride 0) of `bytes` bytes at `base`, in SGPRs.
 // Reads at or beyond `bytes` return zeros.
-__device__ __forceinline__ v4i rsrc(const uint8_t* base, int64_t bytes) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const int nrec = bytes <= 0 ? 0 : (int)bytes;
+__device__ __forceinline__ v4i rsrc(uint64_t b, int bytes) {
+  const int nrec = bytes < 0 ? 0 : bytes;
   return v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)b), (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu),
              __builtin_amdgcn_readfirstlane(nrec), RSRC_W3};
 }
 
 // buffer_load ... lds: each lane's 16 (or 4) bytes at voff land in LDS at
-// lds + 16 (or 4) * lane.  Issued as inline asm so that the compiler does not
+// M0 + 16 (or 4) * lane.  Issued as inline asm so that the compiler does not
 // treat the asynchronous LDS write as aliasing every later LDS read (it would
 // wait for all outstanding loads before each one); completion is tracked
-// explicitly with s_waitcnt vmcnt and published with s_barrier.
-// M0 (the LDS destination) is saved and restored around the instruction.
-__device__ __forceinline__ void dma_x4(const v4i& rs, uint32_t lds, int voff) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "s"(lds), "v"(voff), "s"(rs));
+// explicitly with s_waitcnt vmcnt and published with s_barrier.  A group of
+// loads is bracketed by m0_save / m0_restore (M0 is the LDS destination).
+__device__ __forceinline__ uint32_t m0_save() {
+  uint32_t k;
+  asm volatile("s_mov_b32 %0, m0" : "=s"(k));
+  return k;
 }
-__device__ __forceinline__ void dma_x1(const v4i& rs, uint32_t lds, int voff) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "s"(lds), "v"(voff), "s"(rs));
+__device__ __forceinline__ void m0_restore(uint32_t k) { asm volatile("s_mov_b32 m0, %0" ::"s"(k)); }
+__device__ __forceinline__ void dma_x4(const v4i& rs, uint32_t slot, uint32_t off, int voff) {
+  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds" ::"s"(slot), "s"(off), "v"(voff),
+               "s"(rs)
+               : "scc");
+}
+__device__ __forceinline__ void dma_x1(const v4i& rs, uint32_t slot, uint32_t off, int voff) {
+  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds" ::"s"(slot), "s"(off), "v"(voff),
+               "s"(rs)
+               : "scc");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
@@ -208,84 +209,60 @@ template <int VE> __device__ __forceinline__ void v_chunks(int d, int nb32, int 
   }
 }
 
-// DMA item of a step: source buffer (base, size, bytes per step), LDS offset
-// in the slot, per-lane byte offset.  All but voff are wave-uniform.
+// One DMA load of a step: LDS offset in the slot (padding loads go to the
+// slot's sink) and per-lane byte offset.
 struct Dma {
-  const uint8_t* base;
-  int64_t bytes;
-  int stride;
   int lds;
   int voff;
 };
 
-template <int QK, int VE, int PE, int D>
-struct DmaSrc {
-  const uint8_t *k, *ks, *v, *vs;
-  int64_t kb, ksb, vb, vsb;
-  int ko;  // D = 64: the head's first key scale sits in the upper half of a dword
-  __device__ Dma kc(int lds, int voff) const { return Dma{k, kb, KS * (D * Fmt<QK>::bits / 8), lds, voff}; }
-  __device__ Dma vc(int lds, int voff) const { return Dma{v, vb, 2 * 4 * Fmt<VE>::bits, lds, voff}; }
-  __device__ Dma ksc(int lds, int voff) const { return Dma{ks, ksb, KS * (D / 32), lds, voff}; }
-  __device__ Dma vsc(int lds, int voff) const { return Dma{vs, vsb, 256, lds, voff}; }
-};
+constexpr int OOB_OFF = 0x40000000;  // past every buffer (per-head sizes are below 2^30)
 
+// 16-byte load `it` of the K (kside) or V side for loader lane `lane`
 template <int QK, int VE, int PE, int D>
-__device__ Dma dma16(int item, int lane, int nb32, const DmaSrc<QK, VE, PE, D>& src) {
+__device__ Dma dma16(bool kside, int it, int lane, int nb32) {
   using G = Geo<QK, VE, D>;
   const int hh = lane >> 5, rho = lane & 31;
   int a, b;
-  if (item < G::NK) {
-    const int kg = item / G::DH, dh = item % G::DH;
-    k_chunks<QK, D>(row_key<PE>(kg, rho), dh, hh, a, b);
-    return src.kc(G::K_OFF + item * Opd<QK>::region, a);
+  if (kside) {
+    if (it >= G::N16K) return Dma{G::SINK_OFF, OOB_OFF};
+    const int o = it % G::NK, tail = it / G::NK;
+    k_chunks<QK, D>(row_key<PE>(o / G::DH, rho), o % G::DH, hh, a, b);
+    return Dma{G::K_OFF + o * Opd<QK>::region + 1024 * tail, tail ? b : a};
   }
-  if (item < G::NK + G::NV) {
-    const int o = item - G::NK;
-    v_chunks<VE>(32 * o + rho, nb32, hh, a, b);
-    return src.vc(G::V_OFF + o * Opd<VE>::region, a);
-  }
-  int it = item - G::NK - G::NV;
-  if constexpr (Opd<QK>::tail == 16) {
-    if (it < G::NK) {
-      const int kg = it / G::DH, dh = it % G::DH;
-      k_chunks<QK, D>(row_key<PE>(kg, rho), dh, hh, a, b);
-      return src.kc(G::K_OFF + it * Opd<QK>::region + 1024, b);
-    }
-    it -= G::NK;
-  }
-  v_chunks<VE>(32 * it + rho, nb32, hh, a, b);
-  return src.vc(G::V_OFF + it * Opd<VE>::region + 1024, b);
+  if (it >= G::N16V) return Dma{G::SINK_OFF, OOB_OFF};
+  const int o = it % G::NV, tail = it / G::NV;
+  v_chunks<VE>(32 * o + rho, nb32, hh, a, b);
+  return Dma{G::V_OFF + o * Opd<VE>::region + 1024 * tail, tail ? b : a};
 }
 
+// 4-byte tail load `it`: dword (lane & 1) of the 8-byte FP6 tail of consumer
+// lane L = 32p + (lane >> 1) of operand it/2, p = it & 1
 template <int QK, int VE, int PE, int D>
-__device__ Dma dma4(int item, int lane, int nb32, const DmaSrc<QK, VE, PE, D>& src) {
+__device__ Dma dma4(bool kside, int it, int lane, int nb32) {
   using G = Geo<QK, VE, D>;
-  int it = item;
   int a, b;
-  if constexpr (Opd<QK>::tail == 8) {
-    if (it < 2 * G::NK) {
-      // 8-byte tail of consumer lane L = 32p + (lane >> 1), dword lane & 1
-      const int o = it >> 1, p = it & 1, L = 32 * p + (lane >> 1);
-      const int kg = o / G::DH, dh = o % G::DH;
-      k_chunks<QK, D>(row_key<PE>(kg, L & 31), dh, L >> 5, a, b);
-      return src.kc(G::K_OFF + o * Opd<QK>::region + 1024 + 256 * p, b + 4 * (lane & 1));
-    }
-    it -= 2 * G::NK;
+  if (it >= (kside ? G::NTK : G::NTV)) return Dma{G::SINK_OFF, OOB_OFF};
+  const int o = it >> 1, p = it & 1, L = 32 * p + (lane >> 1);
+  if (kside) {
+    k_chunks<QK, D>(row_key<PE>(o / G::DH, L & 31), o % G::DH, L >> 5, a, b);
+    return Dma{G::K_OFF + o * Opd<QK>::region + 1024 + 256 * p, b + 4 * (lane & 1)};
   }
-  if constexpr (Opd<VE>::tail == 8) {
-    if (it < 2 * G::NV) {
-      const int o = it >> 1, p = it & 1, L = 32 * p + (lane >> 1);
-      v_chunks<VE>(32 * o + (L & 31), nb32, L >> 5, a, b);
-      return src.vc(G::V_OFF + o * Opd<VE>::region + 1024 + 256 * p, b + 4 * (lane & 1));
-    }
-    it -= 2 * G::NV;
+  v_chunks<VE>(32 * o + (L & 31), nb32, L >> 5, a, b);
+  return Dma{G::V_OFF + o * Opd<VE>::region + 1024 + 256 * p, b + 4 * (lane & 1)};
+}
+
+// scale load of a step: wave 0 of each side, padding for the others.  K: lane
+// i = 32 kg + rho loads the scale dword of its key; V: one dword per lane.
+template <int QK, int VE, int PE, int D>
+__device__ Dma dma_scale(bool kside, int wj, int lane, int ko) {
+  using G = Geo<QK, VE, D>;
+  if (wj != 0) return Dma{G::SINK_OFF, OOB_OFF};
+  if (kside) {
+    const int key = row_key<PE>(lane >> 5, lane & 31) + ko;
+    return Dma{G::KS_OFF + 4 * lane, (D == 128) ? key * 4 : (key & ~1) * 2};
   }
-  if (it == 0) {
-    // K scales: lane i = 32 kg + rho loads the scale dword of its key
-    const int key = row_key<PE>(lane >> 5, lane & 31) + src.ko;
-    return src.ksc(G::KS_OFF + 4 * lane, (D == 128) ? key * 4 : (key & ~1) * 2);
-  }
-  return src.vsc(G::VS_OFF + 4 * lane, 4 * lane);
+  return Dma{G::VS_OFF + 4 * lane, 4 * lane};
 }
 
 // E8M0 of a P block from its largest BF16 pattern (integer exponent math)
@@ -320,20 +297,28 @@ __device__ __forceinline__ float max32(const v16f (&S)[2]) { return __builtin_fm
 // P operand from packed patterns and the lane's maxima over key groups 0/1.
 // FP6 P: the lane's 32 keys are one block.  FP8 P: elements 0-15 belong to
 // block 0 of the step, 16-31 to block 1, each block spanning lanes q and q+32.
-template <int PE>
+template <int PE, bool FAST>
 __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, float m1, int lane, v8i& pA, int& pS,
                                          uint32_t (&dsc)[2]) {
   if constexpr (!Opd<PE>::split) {
     const float tm = __builtin_fmaxf(m0, m1);
-    const uint32_t bmax = (tm >= 128.0f) ? min(__float2uint_rz(tm), 0x7F7Fu) : 0u;
-    const uint32_t sc = p_scale<PE>(bmax);
+    uint32_t sc;
+    if constexpr (FAST) {
+      // the block max lies in [PFlush, TgEff]: no flush, clamp or zero code
+      constexpr int thr7 = (int)(Fmt<PE>::mthr23 >> 16);
+      sc = ((__float2uint_rz(tm) + (uint32_t)(127 - thr7)) >> 7) - Fmt<PE>::emax;
+    } else {
+      const uint32_t bmax = (tm >= 128.0f) ? min(__float2uint_rz(tm), 0x7F7Fu) : 0u;
+      sc = p_scale<PE>(bmax);
+    }
     v16u wv;
 #pragma unroll
     for (int i = 0; i < 16; ++i) wv[i] = w[i];
     const v32bf x = __builtin_bit_cast(v32bf, wv);
     v6i r;
-    if constexpr (PE == E2M3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(x, e8m0_to_float(sc));
-    else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(x, e8m0_to_float(sc));
+    const float X = FAST ? __uint_as_float(sc << 23) : e8m0_to_float(sc);
+    if constexpr (PE == E2M3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(x, X);
+    else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(x, X);
     pA = v8i{r[0], r[1], r[2], r[3], r[4], r[5], 0, 0};
     pS = (int)sc;
     dsc[0] = sc;
@@ -385,27 +370,34 @@ __device__ __forceinline__ void dump_p(const FwdArgs& a, int bh, int qq, int k0,
 template <int PE> struct LAcc { typedef v4f T; };
 template <> struct LAcc<E4M3> { typedef v16f T; };
 
+// value of lane `base/4 + k` for a byte address base; base is made opaque
+// first so that the address arithmetic is not hoisted out of the (rare) path
+// that uses it, where it would hold registers for the whole loop
+__device__ __forceinline__ float lane_bcast(float v, int base, int k) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(base + 4 * k, __float_as_int(v)));
+}
+
 // rho of query q is held by lanes q and q+32; O lane (c, h) reg 4i+j holds query 8i+4h+j
 template <int PE, int NV>
 __device__ __forceinline__ void rescale(v16f (&O)[NV], typename LAcc<PE>::T& L, float rho, int lane) {
-  const int h = lane >> 5;
-  float r[16];
+  int base = (lane >> 5) << 4;  // byte address of lane 4h
+  asm volatile("" : "+v"(base));
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[4 * i + j] = wshfl(rho, 8 * i + 4 * h + j);
+    for (int j = 0; j < 4; ++j) {
+      const float r = lane_bcast(rho, base, 8 * i + j);
 #pragma unroll
-  for (int o = 0; o < NV; ++o)
-#pragma unroll
-    for (int k = 0; k < 16; ++k) O[o][k] *= r[k];
-  if constexpr (Opd<PE>::split) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) L[k] *= r[k];
-  } else {
+      for (int o = 0; o < NV; ++o) O[o][4 * i + j] *= r;
+      if constexpr (Opd<PE>::split) L[4 * i + j] *= r;
+    }
+  if constexpr (!Opd<PE>::split) {
     // 16x16 layout: lane (c16, g) reg k holds l of query 4g+k (c16 < 8) or 16+4g+k
     const int c16 = lane & 15, g = (lane >> 4) & 3;
+    int lb = 4 * ((c16 < 8 ? 0 : 16) + 4 * g);
+    asm volatile("" : "+v"(lb));
 #pragma unroll
-    for (int k = 0; k < 4; ++k) L[k] *= wshfl(rho, (c16 < 8 ? 0 : 16) + 4 * g + k);
+    for (int k = 0; k < 4; ++k) L[k] *= lane_bcast(rho, lb, k);
   }
 }
 
@@ -414,7 +406,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   using G = Geo<QK, VE, D>;
   using LT = typename LAcc<PE>::T;
   constexpr int NV = G::NV;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * G::SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -423,63 +415,60 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   const int Sq = a.Sq, Skv = a.Skv, nb32 = a.nb32;
   const int qw0 = blockIdx.x * QWG + w * QW;
   const int ns = (Skv + KS - 1) / KS;
+  const int nklast = Skv - (ns - 1) * KS;     // keys of the last step (1..64)
+  const int upart = nklast < KS ? ns - 1 : -1;  // the last step, when partial
 
-  DmaSrc<QK, VE, PE, D> src;
-  src.k = a.kc + (size_t)bh * Skv * G::QRB;
+  // ---- DMA: this wave's loads (the same every step) and its two running
+  // buffer descriptors (operand codes and scales of its side)
+  const bool kside = w < 4;
+  const int wj = w & 3;
   // K scales are read a dword at a time; for D = 64 (two bytes per key) the
   // head may start in the middle of a dword: read from the dword boundary and
   // shift every key by one
   const size_t ks0 = (size_t)bh * Skv * G::KSB;
-  src.ko = (D == 64) ? (int)((ks0 >> 1) & 1) : 0;
-  src.ks = a.ks + (ks0 & ~(size_t)3);
-  src.v = a.vc + (size_t)bh * D * nb32 * G::VBB;
-  src.vs = a.vs + (size_t)bh * nb32 * 128;
-  src.kb = (int64_t)Skv * G::QRB;
-  src.ksb = ((int64_t)(Skv + src.ko) * G::KSB + 3) & ~(int64_t)3;
-  src.vb = (int64_t)D * nb32 * G::VBB;
-  src.vsb = (int64_t)nb32 * 128;
-
-  // ---- this wave's DMA items (the same every step)
-  Dma d16[G::M16], d4[G::M4];
-  int n16 = 0, n4 = 0;
+  const int ko = (D == 64) ? (int)((ks0 >> 1) & 1) : 0;
+  int l16[G::M16], v16[G::M16], lt[G::MT > 0 ? G::MT : 1], vt[G::MT > 0 ? G::MT : 1];
 #pragma unroll
   for (int k = 0; k < G::M16; ++k) {
-    const int it = w + NW * k;
-    if (it < G::N16) {
-      d16[k] = dma16<QK, VE, PE, D>(it, lane, nb32, src);
-      ++n16;
-    } else {
-      d16[k] = Dma{src.k, 0, 0, 0, 0};
-    }
+    const Dma d = dma16<QK, VE, PE, D>(kside, wj + 4 * k, lane, nb32);
+    l16[k] = __builtin_amdgcn_readfirstlane(d.lds);
+    v16[k] = d.voff;
   }
 #pragma unroll
-  for (int k = 0; k < G::M4; ++k) {
-    const int it = w + NW * k;
-    if (it < G::N4) {
-      d4[k] = dma4<QK, VE, PE, D>(it, lane, nb32, src);
-      ++n4;
-    } else {
-      d4[k] = Dma{src.k, 0, 0, 0, 0};
-    }
+  for (int k = 0; k < G::MT; ++k) {
+    const Dma d = dma4<QK, VE, PE, D>(kside, wj + 4 * k, lane, nb32);
+    lt[k] = __builtin_amdgcn_readfirstlane(d.lds);
+    vt[k] = d.voff;
   }
-  const int nper = n16 + n4;
+  const Dma dsl = dma_scale<QK, VE, PE, D>(kside, wj, lane, ko);
+  const int lsc = __builtin_amdgcn_readfirstlane(dsl.lds), vsc_off = dsl.voff;
+  uint64_t cbase = kside ? (uint64_t)(uintptr_t)(a.kc + (size_t)bh * Skv * G::QRB)
+                         : (uint64_t)(uintptr_t)(a.vc + (size_t)bh * D * nb32 * G::VBB);
+  int crem = kside ? Skv * G::QRB : D * nb32 * G::VBB;
+  const int cstride = kside ? KS * G::QRB : 2 * G::VBB;
+  uint64_t sbase = kside ? (uint64_t)(uintptr_t)(a.ks + (ks0 & ~(size_t)3))
+                         : (uint64_t)(uintptr_t)(a.vs + (size_t)bh * nb32 * 128);
+  int srem = kside ? (((Skv + ko) * G::KSB + 3) & ~3) : nb32 * 128;
+  const int sstride = kside ? KS * G::KSB : 256;
+  int snext = 0;  // next step to fetch
+  const uint32_t lds0 = lds_addr(smem);
 
-  auto issue = [&](int s) {
-    const uint8_t* slot = smem + (s % NS) * G::SLOT;
+  // loads of step snext into its slot; past the last step they read zeros
+  auto issue = [&]() {
+    const uint32_t slot = lds0 + (uint32_t)((snext & (NS - 1)) * G::SLOT);
+    const v4i rc = rsrc(cbase, crem), rs = rsrc(sbase, srem);
+    const uint32_t keep = m0_save();
 #pragma unroll
-    for (int k = 0; k < G::M16; ++k) {
-      if (k < n16) {
-        const int64_t off = (int64_t)s * d16[k].stride;
-        dma_x4(rsrc(d16[k].base + off, d16[k].bytes - off), lds_addr(slot + d16[k].lds), d16[k].voff);
-      }
-    }
+    for (int k = 0; k < G::M16; ++k) dma_x4(rc, slot, (uint32_t)l16[k], v16[k]);
 #pragma unroll
-    for (int k = 0; k < G::M4; ++k) {
-      if (k < n4) {
-        const int64_t off = (int64_t)s * d4[k].stride;
-        dma_x1(rsrc(d4[k].base + off, d4[k].bytes - off), lds_addr(slot + d4[k].lds), d4[k].voff);
-      }
-    }
+    for (int k = 0; k < G::MT; ++k) dma_x1(rc, slot, (uint32_t)lt[k], vt[k]);
+    dma_x1(rs, slot, (uint32_t)lsc, vsc_off);
+    m0_restore(keep);
+    cbase += (uint64_t)cstride;
+    crem -= cstride;
+    sbase += (uint64_t)sstride;
+    srem -= sstride;
+    ++snext;
   };
 
   // ---- Q operands (B of the score product) and their scales
@@ -512,7 +501,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   int ksh[2];
 #pragma unroll
   for (int kg = 0; kg < 2; ++kg) {
-    const int key = row_key<PE>(kg, n) + src.ko;
+    const int key = row_key<PE>(kg, n) + ko;
     ksh[kg] = (D == 128) ? 8 * hh : 16 * (key & 1) + 8 * hh;
   }
   // ones operand of the l product.  FP6 P (16x16x128, lanes read as rows
@@ -529,7 +518,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   }
 
   const float T0 = a.T0, Tg = a.Tg;
-  const float TgEff = fminf(Tg, 32639.0f);  // above this the stage-1 clamp could act: exact path
+  // above TgEff the stage-1 clamp could act: exact path (kept in an SGPR)
+  const float TgEff = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fminf(Tg, 32639.0f))));
 
   float C = 0.0f;
   v16f Cv;  // C splat: the accumulator's initial value of the score product
@@ -551,7 +541,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   for (int k = 0; k < (int)(sizeof(LT) / 4); ++k) L[k] = 0.0f;
 
   auto scores = [&](v16f (&S)[2], int s) {
-    const uint8_t* slot = smem + (s % NS) * G::SLOT;
+    const uint8_t* slot = smem + (s & (NS - 1)) * G::SLOT;
     const uint32_t kd0 = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 4 * n) >> ksh[0];
     const uint32_t kd1 = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 128 + 4 * n) >> ksh[1];
     // both key groups' first feature half (initial value C), then the second
@@ -569,7 +559,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       }
   };
   auto pv = [&](const v8i& pA, int pS, int s) {
-    const uint8_t* slot = smem + (s % NS) * G::SLOT;
+    const uint8_t* slot = smem + (s & (NS - 1)) * G::SLOT;
     const int vsc = *reinterpret_cast<const int*>(slot + G::VS_OFF + 4 * lane);
 #pragma unroll
     for (int o = 0; o < NV; ++o) {
@@ -599,42 +589,31 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) S[kg][k] = S[kg][k] + d;
   };
+  // 128-key gate tile: the lane's maximum over the odd step s of the tile,
+  // with the current offset (its scores are recomputed on step s itself)
+  auto ahead_max = [&](int s) -> float {
+    v16f Sn[2];
+    scores(Sn, s);
+    if (s == upart) mask(Sn, nklast);
+    return max32(Sn);
+  };
 
-  // ---- prologue: fetch PF steps and make steps 0 and 1 visible
-  const int npro = min(PF, ns);
-  for (int s = 0; s < npro; ++s) issue(s);
-  wait_steps(nper, npro == PF);
-  barrier();
-
-  v16f S[2];
-  [[maybe_unused]] v16f Sn[2];  // kv_tile 128: scores of the second half of the gate tile
   v8i pA = {0, 0, 0, 0, 0, 0, 0, 0};
   int pS = 127;
+  // gate outcome of the last conversion: O and l are rescaled by rho (per
+  // query) before the PV product of that step when any query of the wave fired
+  float rho = 1.0f;
+  bool any_fire = false;
+  auto apply_gate = [&]() {
+    if (any_fire) rescale<PE, NV>(O, L, rho, lane);
+  };
 
-  for (int u = 0; u < ns; ++u) {
-    if (u > 0) {
-      wait_steps(nper, ns - 2 - u >= PF - 2);
-      barrier();
-    }
-    if (u + PF < ns) issue(u + PF);
-    const bool even = (u & 1) == 0;
-    const bool has_next = u + 1 < ns;
-    if constexpr (KV128) {
-      if (even) {
-        scores(S, u);
-        if (has_next) scores(Sn, u + 1);
-      } else {
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg) S[kg] = Sn[kg];
-      }
-    } else {
-      scores(S, u);
-    }
-    if (u > 0) pv(pA, pS, u - 1);
-
-    // ---- stage 1 + 2 on step u
-    const int k0 = u * KS;
-    const int nk = min(KS, Skv - k0);
+  // Stage 1 + 2 of step u from its scores S; mnext: ahead_max of step u + 1
+  // when u starts a 128-key gate tile.  FIRST: step 0 (sets the reference).
+  // Sets pA/pS, and rho/any_fire for apply_gate.
+  auto convert = [&](v16f (&S)[2], int u, float mnext, auto first_t) {
+    constexpr bool FIRST = decltype(first_t)::value;
+    const bool pair = KV128 && (u & 1) == 0 && u + 1 < ns;
     uint32_t wv[16];
     pack_b(S, wv);
     const float m0 = max16(S[0]), m1 = max16(S[1]);
@@ -648,45 +627,34 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       lo = tm;
     }
     if constexpr (KV128) {
-      if (even && has_next) tm = __builtin_fmaxf(tm, max32(Sn));
+      if (pair) tm = __builtin_fmaxf(tm, mnext);
     }
-    const bool bad = !(tm <= TgEff) || !(lo >= PFlush<PE>::t);
-    const bool rare = (u == 0) || (nk < KS) || (__ballot(bad) != 0);
+    // fast path iff PFlush <= every block max and the tile max <= TgEff
+    const bool ok = __builtin_fminf(TgEff - tm, lo - PFlush<PE>::t) >= 0.0f;
+    const bool rare = FIRST || u == upart || (__ballot(!ok) != 0);
     uint32_t dsc[2];
+    rho = 1.0f;
+    any_fire = false;
     if (!rare) {
-      p_from_w<PE>(wv, m0, m1, lane, pA, pS, dsc);
+      p_from_w<PE, true>(wv, m0, m1, lane, pA, pS, dsc);
     } else {
       // ---- exact path: masking, reference, gate, flush and clamp
-      mask(S, nk);
+      if (u == upart) mask(S, nklast);
       float m = max32(S);
-      m = __builtin_fmaxf(m, wshfl(m, lane ^ 32));
-      bool pair = false;  // the gate tile spans steps u and u+1
       if constexpr (KV128) {
-        pair = even && has_next;
-        if (pair) {
-          mask(Sn, min(KS, Skv - k0 - KS));
-          float mn = max32(Sn);
-          m = __builtin_fmaxf(m, __builtin_fmaxf(mn, wshfl(mn, lane ^ 32)));
-        }
+        if (pair) m = __builtin_fmaxf(m, mnext);
       }
-      float rho = 1.0f;
-      bool any_fire = false;
-      if (u == 0) {
+      m = __builtin_fmaxf(m, wshfl(m, lane ^ 32));
+      if (FIRST) {
         set_C(T0 - m);
         shift(S, C);
-        if constexpr (KV128) {
-          if (pair) shift(Sn, C);
-        }
-      } else if (!KV128 || even) {
+      } else if (!KV128 || (u & 1) == 0) {
         const bool fire = m > Tg;
         const float delta = fire ? m - T0 : 0.0f;
         if (fire) {
           shift(S, -delta);
           cnt += 1;
           rho = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
-          if constexpr (KV128) {
-            if (pair) shift(Sn, -delta);
-          }
         }
         any_fire = __ballot(fire) != 0;
         if (any_fire) set_C(C - delta);
@@ -703,12 +671,81 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
           else mx1 = __builtin_fmaxf(mx1, f);
         }
       pack_b(S, wv);
-      p_from_w<PE>(wv, mx0, mx1, lane, pA, pS, dsc);
-      if (any_fire) rescale<PE, NV>(O, L, rho, lane);
+      p_from_w<PE, false>(wv, mx0, mx1, lane, pA, pS, dsc);
     }
-    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, k0, hh, pA, dsc);
+    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, u * KS, hh, pA, dsc);
+  };
+
+  // one barrier per step: before it each wave waits for its loads of the
+  // steps up to u + 1; after it the loads of step u + PF go into the slot of
+  // step u - 2, which every wave finished reading before the barrier
+  auto sync = [&]() {
+    wait_vm<(PF - 2) * G::PER_WAVE>();
+    barrier();
+    issue();
+  };
+  // end of the matrix phase of waves 0-3: the PV products are issued here,
+  // not sunk past the conversion (which would put both waves of a SIMD on
+  // the matrix core at once)
+  auto phase = [&]() {
+#pragma unroll
+    for (int o = 0; o < NV; ++o) asm volatile("" : "+v"(O[o]));
+    asm volatile("" : "+v"(L));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto next_max = [&](int u) -> float {
+    if constexpr (KV128) {
+      if ((u & 1) == 0 && u + 1 < ns) return ahead_max(u + 1);
+    }
+    return 0.0f;
+  };
+
+  for (int s = 0; s < PF; ++s) issue();
+  v16f S[2];
+  if (kside) {
+    // waves 0-3: [barrier] scores(u), PV(u-1), convert(u)
+    sync();
+    float mn = next_max(0);
+    scores(S, 0);
+    convert(S, 0, mn, std::true_type{});
+    for (int u = 1; u < ns; ++u) {
+      sync();
+      mn = next_max(u);
+      scores(S, u);
+      pv(pA, pS, u - 1);
+      phase();
+      convert(S, u, mn, std::false_type{});
+      apply_gate();
+    }
+    pv(pA, pS, ns - 1);
+  } else {
+    // waves 4-7: [barrier] convert(u-1), scores(u), PV(u-1)
+    sync();
+    float mn = next_max(0);
+    scores(S, 0);
+    if (ns > 1) {
+      sync();
+      convert(S, 0, mn, std::true_type{});
+      mn = next_max(1);
+      scores(S, 1);
+      pv(pA, pS, 0);
+      for (int u = 2; u < ns; ++u) {
+        sync();
+        convert(S, u - 1, mn, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        mn = next_max(u);
+        scores(S, u);
+        apply_gate();
+        pv(pA, pS, u - 1);
+      }
+      convert(S, ns - 1, mn, std::false_type{});
+      apply_gate();
+    } else {
+      convert(S, 0, mn, std::true_type{});
+    }
+    pv(pA, pS, ns - 1);
   }
-  pv(pA, pS, ns - 1);
+  wait_vm<0>();  // loads past the end are still in flight
 
   // ---- epilogue: O / l -> bf16; counts
   float lq[16];
