@@ -286,6 +286,13 @@ __device__ __forceinline__ void pack_b(const v16f (&S)[2], uint32_t (&w)[16]) {
   }
 }
 
+// half of pack_b: key group kg (patterns 8 kg .. 8 kg + 7)
+__device__ __forceinline__ void pack_half(const v16f (&S)[2], uint32_t (&w)[16], int kg) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    w[8 * kg + i] = __builtin_amdgcn_perm(__float2uint_rz(S[kg][2 * i + 1]), __float2uint_rz(S[kg][2 * i]), 0x05040100u);
+}
+
 __device__ __forceinline__ float max16(const v16f& s) {
   float m = max3f(s[0], s[1], s[2]);
 #pragma unroll
@@ -452,11 +459,20 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   const int sstride = kside ? KS * G::KSB : 256;
   int snext = 0;  // next step to fetch
   const uint32_t lds0 = lds_addr(smem);
+  // the two descriptors live in SGPRs and move by one step per issue
+  v4i rc = rsrc(cbase, crem), rs = rsrc(sbase, srem);
+  auto advance = [](v4i& d, int& rem, int stride) {
+    uint64_t b = ((uint64_t)(uint32_t)d[1] << 32) | (uint32_t)d[0];
+    b += (uint64_t)stride;
+    d[0] = (int)(uint32_t)b;
+    d[1] = (int)(uint32_t)(b >> 32);
+    rem -= stride;
+    d[2] = rem > 0 ? rem : 0;
+  };
 
   // loads of step snext into its slot; past the last step they read zeros
   auto issue = [&]() {
     const uint32_t slot = lds0 + (uint32_t)((snext & (NS - 1)) * G::SLOT);
-    const v4i rc = rsrc(cbase, crem), rs = rsrc(sbase, srem);
     const uint32_t keep = m0_save();
 #pragma unroll
     for (int k = 0; k < G::M16; ++k) dma_x4(rc, slot, (uint32_t)l16[k], v16[k]);
@@ -464,10 +480,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     for (int k = 0; k < G::MT; ++k) dma_x1(rc, slot, (uint32_t)lt[k], vt[k]);
     dma_x1(rs, slot, (uint32_t)lsc, vsc_off);
     m0_restore(keep);
-    cbase += (uint64_t)cstride;
-    crem -= cstride;
-    sbase += (uint64_t)sstride;
-    srem -= sstride;
+    advance(rc, crem, cstride);
+    advance(rs, srem, sstride);
     ++snext;
   };
 
@@ -540,41 +554,67 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int k = 0; k < (int)(sizeof(LT) / 4); ++k) L[k] = 0.0f;
 
-  auto scores = [&](v16f (&S)[2], int s) {
+  // K operands of a step (and the lane's two K block-scale words), read from
+  // the LDS ring ahead of the score product that uses them
+  struct KOps {
+    v8i op[2 * G::DH];
+    uint32_t kd[2];
+  };
+  auto read_k = [&](int s) -> KOps {
     const uint8_t* slot = smem + (s & (NS - 1)) * G::SLOT;
-    const uint32_t kd0 = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 4 * n) >> ksh[0];
-    const uint32_t kd1 = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 128 + 4 * n) >> ksh[1];
-    // both key groups' first feature half (initial value C), then the second
+    KOps k;
+    k.kd[0] = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 4 * n) >> ksh[0];
+    k.kd[1] = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 128 + 4 * n) >> ksh[1];
+#pragma unroll
+    for (int i = 0; i < 2 * G::DH; ++i) k.op[i] = lds_operand<QK>(slot + G::K_OFF + i * Opd<QK>::region, lane);
+    return k;
+  };
+  // S^T = K Q^T + C for the 64 keys of a step: both key groups' first
+  // feature half (initial value C), then the second
+  auto scores_of = [&](v16f (&S)[2], const KOps& k) {
 #pragma unroll
     for (int dh = 0; dh < G::DH; ++dh)
 #pragma unroll
       for (int kg = 0; kg < 2; ++kg) {
-        const int ksc = (int)(kg ? kd1 : kd0);
-        const v8i ka = lds_operand<QK>(slot + G::K_OFF + (kg * G::DH + dh) * Opd<QK>::region, lane);
+        const int ksc = (int)k.kd[kg];
+        const v8i& ka = k.op[kg * G::DH + dh];
         if (dh == 0)
           S[kg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qB[0], Cv, QK, QK, 0, ksc, 0, qS[0]);
         else
           S[kg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qB[G::DH - 1], S[kg], QK, QK, 2, ksc, 0,
                                                                   qS[G::DH - 1]);
       }
+    // Cv stays live past the products, so neither of them is selected in the
+    // form that accumulates in place over Cv (which costs a copy of Cv)
+    asm volatile("" ::"v"(Cv));
   };
-  auto pv = [&](const v8i& pA, int pS, int s) {
+  auto scores = [&](v16f (&S)[2], int s) { scores_of(S, read_k(s)); };
+  // V operands of a step and the lane's V scale word, read ahead of the PV
+  // product that uses them
+  struct VOps {
+    v8i op[NV];
+    int vsc;
+  };
+  auto read_v = [&](int s) -> VOps {
     const uint8_t* slot = smem + (s & (NS - 1)) * G::SLOT;
-    const int vsc = *reinterpret_cast<const int*>(slot + G::VS_OFF + 4 * lane);
+    VOps v;
+    v.vsc = *reinterpret_cast<const int*>(slot + G::VS_OFF + 4 * lane);
 #pragma unroll
-    for (int o = 0; o < NV; ++o) {
-      const v8i vb = lds_operand<VE>(slot + G::V_OFF + o * Opd<VE>::region, lane);
-      if (o == 0) O[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, vb, O[0], PE, VE, 0, pS, 0, vsc);
-      if (o == 1) O[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, vb, O[1], PE, VE, 0, pS, 1, vsc);
-      if constexpr (NV > 2) {
-        if (o == 2) O[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, vb, O[2], PE, VE, 0, pS, 2, vsc);
-        if (o == 3) O[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, vb, O[3], PE, VE, 0, pS, 3, vsc);
-      }
+    for (int o = 0; o < NV; ++o) v.op[o] = lds_operand<VE>(slot + G::V_OFF + o * Opd<VE>::region, lane);
+    return v;
+  };
+  // O += P V (feature block o) and l += P 1
+  auto pv_of = [&](const v8i& pa, int ps, const VOps& v) {
+    O[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, v.op[0], O[0], PE, VE, 0, ps, 0, v.vsc);
+    O[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, v.op[1], O[1], PE, VE, 0, ps, 1, v.vsc);
+    if constexpr (NV > 2) {
+      O[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, v.op[2], O[2], PE, VE, 0, ps, 2, v.vsc);
+      O[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, v.op[3], O[3], PE, VE, 0, ps, 3, v.vsc);
     }
     if constexpr (Opd<PE>::split)
-      L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pA, ones, L, PE, E4M3, 0, pS, 0, 127);
+      L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, ones, L, PE, E4M3, 0, ps, 0, 127);
     else
-      L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pA, ones, L, PE, E2M1, 0, pS, 0, 127);
+      L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa, ones, L, PE, E2M1, 0, ps, 0, 127);
   };
   auto mask = [&](v16f (&S)[2], int nk) {
 #pragma unroll
@@ -600,22 +640,15 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
 
   v8i pA = {0, 0, 0, 0, 0, 0, 0, 0};
   int pS = 127;
-  // gate outcome of the last conversion: O and l are rescaled by rho (per
-  // query) before the PV product of that step when any query of the wave fired
-  float rho = 1.0f;
-  bool any_fire = false;
-  auto apply_gate = [&]() {
-    if (any_fire) rescale<PE, NV>(O, L, rho, lane);
-  };
 
-  // Stage 1 + 2 of step u from its scores S; mnext: ahead_max of step u + 1
-  // when u starts a 128-key gate tile.  FIRST: step 0 (sets the reference).
-  // Sets pA/pS, and rho/any_fire for apply_gate.
-  auto convert = [&](v16f (&S)[2], int u, float mnext, auto first_t) {
-    constexpr bool FIRST = decltype(first_t)::value;
-    const bool pair = KV128 && (u & 1) == 0 && u + 1 < ns;
-    uint32_t wv[16];
-    pack_b(S, wv);
+  // fast-path test of step u: the lane's maxima over its two key groups, and
+  // whether every block max is >= PFlush and the gate-tile max <= TgEff
+  // (mnext: the maximum of step u + 1 when u starts a 128-key gate tile)
+  struct Check {
+    float m0, m1;
+    bool ok;
+  };
+  auto check = [&](const v16f (&S)[2], int u, float mnext) -> Check {
     const float m0 = max16(S[0]), m1 = max16(S[1]);
     float tm, lo;
     if constexpr (Opd<PE>::split) {
@@ -627,124 +660,140 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       lo = tm;
     }
     if constexpr (KV128) {
-      if (pair) tm = __builtin_fmaxf(tm, mnext);
+      if ((u & 1) == 0 && u + 1 < ns) tm = __builtin_fmaxf(tm, mnext);
     }
-    // fast path iff PFlush <= every block max and the tile max <= TgEff
-    const bool ok = __builtin_fminf(TgEff - tm, lo - PFlush<PE>::t) >= 0.0f;
-    const bool rare = FIRST || u == upart || (__ballot(!ok) != 0);
-    uint32_t dsc[2];
+    return Check{m0, m1, __builtin_fminf(TgEff - tm, lo - PFlush<PE>::t) >= 0.0f};
+  };
+
+  // exact conversion of step u: masking, reference (FIRST: step 0), gate,
+  // flush and clamp; sets pA/pS and the gate outcome (rho, any_fire)
+  float rho = 1.0f;
+  bool any_fire = false;
+  auto exact = [&](v16f (&S)[2], int u, float mnext, uint32_t (&dsc)[2], auto first_t) {
+    constexpr bool FIRST = decltype(first_t)::value;
+    if (u == upart) mask(S, nklast);
+    float m = max32(S);
+    if constexpr (KV128) {
+      if ((u & 1) == 0 && u + 1 < ns) m = __builtin_fmaxf(m, mnext);
+    }
+    m = __builtin_fmaxf(m, wshfl(m, lane ^ 32));
     rho = 1.0f;
     any_fire = false;
-    if (!rare) {
-      p_from_w<PE, true>(wv, m0, m1, lane, pA, pS, dsc);
-    } else {
-      // ---- exact path: masking, reference, gate, flush and clamp
-      if (u == upart) mask(S, nklast);
-      float m = max32(S);
-      if constexpr (KV128) {
-        if (pair) m = __builtin_fmaxf(m, mnext);
+    if (FIRST) {
+      set_C(T0 - m);
+      shift(S, C);
+    } else if (!KV128 || (u & 1) == 0) {
+      const bool fire = m > Tg;
+      const float delta = fire ? m - T0 : 0.0f;
+      if (fire) {
+        shift(S, -delta);
+        cnt += 1;
+        rho = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
       }
-      m = __builtin_fmaxf(m, wshfl(m, lane ^ 32));
-      if (FIRST) {
-        set_C(T0 - m);
-        shift(S, C);
-      } else if (!KV128 || (u & 1) == 0) {
-        const bool fire = m > Tg;
-        const float delta = fire ? m - T0 : 0.0f;
-        if (fire) {
-          shift(S, -delta);
-          cnt += 1;
-          rho = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
-        }
-        any_fire = __ballot(fire) != 0;
-        if (any_fire) set_C(C - delta);
-      }
-      float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const float v = S[kg][k];
-          const float f = (v >= 128.0f) ? __builtin_fminf(v, 32639.5f) : -INFINITY;
-          S[kg][k] = f;
-          if (kg == 0) mx0 = __builtin_fmaxf(mx0, f);
-          else mx1 = __builtin_fmaxf(mx1, f);
-        }
-      pack_b(S, wv);
-      p_from_w<PE, false>(wv, mx0, mx1, lane, pA, pS, dsc);
+      any_fire = __ballot(fire) != 0;
+      if (any_fire) set_C(C - delta);
     }
-    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, u * KS, hh, pA, dsc);
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float v = S[kg][k];
+        const float f = (v >= 128.0f) ? __builtin_fminf(v, 32639.5f) : -INFINITY;
+        S[kg][k] = f;
+        if (kg == 0) mx0 = __builtin_fmaxf(mx0, f);
+        else mx1 = __builtin_fmaxf(mx1, f);
+      }
+    uint32_t wv[16];
+    pack_b(S, wv);
+    p_from_w<PE, false>(wv, mx0, mx1, lane, pA, pS, dsc);
   };
 
   // one barrier per step: before it each wave waits for its loads of the
-  // steps up to u + 1; after it the loads of step u + PF go into the slot of
+  // steps up to u + 1 (u + 2 with 128-key gate tiles, whose odd step is read
+  // one step early); after it the loads of step u + PF go into the slot of
   // step u - 2, which every wave finished reading before the barrier
   auto sync = [&]() {
-    wait_vm<(PF - 2) * G::PER_WAVE>();
+    wait_vm<(KV128 ? PF - 3 : PF - 2) * G::PER_WAVE>();
     barrier();
     issue();
   };
-  // end of the matrix phase of waves 0-3: the PV products are issued here,
-  // not sunk past the conversion (which would put both waves of a SIMD on
-  // the matrix core at once)
-  auto phase = [&]() {
-#pragma unroll
-    for (int o = 0; o < NV; ++o) asm volatile("" : "+v"(O[o]));
-    asm volatile("" : "+v"(L));
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto next_max = [&](int u) -> float {
+  // scores of step s (and, when s starts a 128-key gate tile, the maximum of
+  // step s + 1 with the same offset)
+  float mn = 0.0f;
+  auto next_scores = [&](v16f (&S)[2], int s) {
     if constexpr (KV128) {
-      if ((u & 1) == 0 && u + 1 < ns) return ahead_max(u + 1);
+      if ((s & 1) == 0 && s + 1 < ns) mn = ahead_max(s + 1);
     }
-    return 0.0f;
+    scores(S, s);
   };
+  // keep a value computed in a branch inside that branch (the compiler
+  // would otherwise sink the producing matrix instructions past the merge)
+  auto pin16 = [](v16f& x) { asm volatile("" : "+v"(x)); };
 
   for (int s = 0; s < PF; ++s) issue();
   v16f S[2];
-  if (kside) {
-    // waves 0-3: [barrier] scores(u), PV(u-1), convert(u)
-    sync();
-    float mn = next_max(0);
-    scores(S, 0);
-    convert(S, 0, mn, std::true_type{});
-    for (int u = 1; u < ns; ++u) {
-      sync();
-      mn = next_max(u);
-      scores(S, u);
-      pv(pA, pS, u - 1);
-      phase();
-      convert(S, u, mn, std::false_type{});
-      apply_gate();
-    }
-    pv(pA, pS, ns - 1);
-  } else {
-    // waves 4-7: [barrier] convert(u-1), scores(u), PV(u-1)
-    sync();
-    float mn = next_max(0);
-    scores(S, 0);
-    if (ns > 1) {
-      sync();
-      convert(S, 0, mn, std::true_type{});
-      mn = next_max(1);
-      scores(S, 1);
-      pv(pA, pS, 0);
-      for (int u = 2; u < ns; ++u) {
-        sync();
-        convert(S, u - 1, mn, std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        mn = next_max(u);
-        scores(S, u);
-        apply_gate();
-        pv(pA, pS, u - 1);
-      }
-      convert(S, ns - 1, mn, std::false_type{});
-      apply_gate();
-    } else {
-      convert(S, 0, mn, std::true_type{});
-    }
-    pv(pA, pS, ns - 1);
+  sync();
+  next_scores(S, 0);
+  {
+    uint32_t dsc[2];
+    exact(S, 0, mn, dsc, std::true_type{});
+    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, 0, hh, pA, dsc);
   }
+  // V operands are read a phase ahead except with FP8 P (FP8 V operands
+  // are 8 registers each; there the registers are not available)
+  constexpr bool PRE_V = !Opd<PE>::split;
+  constexpr bool PRE_K = !Opd<QK>::split;  // the same for FP8 K operands
+  VOps vop;
+  if constexpr (PRE_V) vop = read_v(0);
+  next_scores(S, 1);
+  // step u: the K operands of step u + 1 are read while the PV products of
+  // step u - 1 run on the matrix core and the VALU converts the scores of
+  // step u (along the fast path always: on a rare step the exact path
+  // overwrites its result); then the V operands of step u are read and the
+  // score product of step u + 1 is issued.  Operand reads thus have a whole
+  // phase of the step to arrive.
+  for (int u = 1; u < ns; ++u) {
+    sync();
+    KOps kop;
+    if constexpr (PRE_K) kop = read_k(u + 1);
+    if constexpr (PRE_V) pv_of(pA, pS, vop);
+    else pv_of(pA, pS, read_v(u - 1));
+    const Check c = check(S, u, mn);
+    const bool rare = (u == upart) | (__ballot(!c.ok) != 0);
+    uint32_t wv[16], dsc[2];
+    pack_b(S, wv);
+    v8i pAf;
+    int pSf;
+    p_from_w<PE, true>(wv, c.m0, c.m1, lane, pAf, pSf, dsc);
+    // computed here on every step (not sunk into the fast branch)
+    asm volatile("" : "+v"(pAf), "+v"(pSf));
+#pragma unroll
+    for (int o = 0; o < NV; ++o) pin16(O[o]);
+    asm volatile("" : "+v"(L));
+    // one PV product per group of VALU work
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * G::DH + 2, 0);
+#pragma unroll
+    for (int i = 0; i < NV + 1; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 15, 0);
+    }
+    pA = pAf;
+    pS = pSf;
+    if (rare) {
+      exact(S, u, mn, dsc, std::false_type{});
+      if (any_fire) rescale<PE, NV>(O, L, rho, lane);
+    }
+    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, u * KS, hh, pA, dsc);
+    if constexpr (PRE_V) vop = read_v(u);
+    if constexpr (KV128) {
+      if (((u + 1) & 1) == 0 && u + 2 < ns) mn = ahead_max(u + 2);
+    }
+    if constexpr (PRE_K) scores_of(S, kop);
+    else scores_of(S, read_k(u + 1));
+  }
+  if constexpr (PRE_V) pv_of(pA, pS, vop);
+  else pv_of(pA, pS, read_v(ns - 1));
   wait_vm<0>();  // loads past the end are still in flight
 
   // ---- epilogue: O / l -> bf16; counts
