@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from softmax_matrix_cores_amd import workloads as W
-from tests.gpu_util import assert_ok, run_case
+from tests.gpu_util import assert_ok, check_p, run_case
 
 pytestmark = pytest.mark.gpu
 
@@ -47,11 +47,12 @@ def test_tau_sweep(oracle, tau, elems):
     w = W.custom("stress-mxfp8", name=f"tau{tau}-{qk}", B=1, H=2, Sq=96, Skv=520, D=128, seed=21, qk_elem=qk,
                  v_elem=ve, p_elem=pe)
     res = run_case(oracle, w, dump_head=(0, 1), dump_rows=(0, 32), tau=tau)
-    assert_ok(res)
+    assert_ok(res, defer_p=True)
     if tau == 0.0:
         assert res["total_counts"] > 0
     if tau == 1e4:
         assert res["total_counts"] == 0
+    check_p(res)
 
 
 def test_tiny_mxfp8_full(oracle):
@@ -64,7 +65,8 @@ def test_stress_mxfp8_full(oracle):
     w = W.WORKLOADS["stress-mxfp8"]
     res = run_case(oracle, w, dump_head=(0, 3), dump_rows=(0, w.Sq))
     assert res["total_counts"] > 0
-    assert_ok(res)
+    assert_ok(res, defer_p=True)
+    check_p(res)
 
 
 @pytest.mark.parametrize("name", ["qknorm-mxfp6", "qknorm-mxfp4", "video-mxfp6", "video-mxfp4"])
