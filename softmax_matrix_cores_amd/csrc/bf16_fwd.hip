@@ -5,174 +5,308 @@
 // paragraph 8) and describe the conventional scheme as repeatedly updating a
 // reference maximum and rescaling the accumulated results when it grows
 // (paragraph 5).  This kernel is that scheme, FlashAttention style:
-//   per 64-key tile: s = q.k (BF16 MFMA, fp32 accumulate), running max m,
-//   p = exp2(s*sigma*log2e - m'), O and l rescaled by exp2(m_old - m_new),
-//   O += bf16(p) V (BF16 MFMA), l += sum p; finally O / l.
+//   per 64-key step: s = q.k (BF16 MFMA, fp32 accumulate), running max m of
+//   s*sigma*log2e, p = exp2(s*sigma*log2e - m), O and l rescaled by
+//   exp2(m_old - m_new) when the max grows, O += bf16(p) V (BF16 MFMA),
+//   l += sum p; finally O / l.
 //
-// Layout (v_mfma_f32_16x16x32_bf16: lane (r = l%16, g = l/16) holds row r,
-// K elements [8g, 8g+8); accumulator lane (n, g) holds rows 4g..4g+3 of
-// column n).  Scores are computed transposed, S^T = K Q^T, with the K rows of
-// each MFMA permuted so that lane (n, g) receives keys 8g..8g+7 of every
-// 32-key chunk for query n -- exactly its A operand of the PV product.
+// Mapping to CDNA4 (v_mfma_f32_32x32x16_bf16: lane (r = l%32, h = l/32) holds
+// row r, K elements [8h, 8h+8); accumulator lane (c, h) register 4i+j holds
+// row 8i+4h+j of column c):
+//   * 8 waves per workgroup, 32 queries per wave.  S^T = K Q^T is computed
+//     with the K rows of each product permuted so that lane (q, h) receives
+//     keys 16t + 8h .. 16t + 8h + 7 of every 16-key chunk t: exactly its A
+//     operand of the PV product (no shuffles).
+//   * K is streamed by LDS DMA into a 4-slot ring in operand order (one
+//     lane-contiguous ds_read_b128 per operand).  V is streamed row-major
+//     into a 3-slot staging ring, and the workgroup transposes each step once
+//     (4x4 blocks of 16-bit elements in registers) into V^T operands in
+//     operand order, double buffered.  Loads run three steps ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace fsattn {
+namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef float v4f_b __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf_b __attribute__((ext_vector_type(2)));
 
-constexpr int BNW = 4;   // waves
-constexpr int BQW = 16;  // queries per wave
-constexpr int BKT = 64;  // keys per tile
+constexpr int BW = 8;         // waves per workgroup
+constexpr int BQ = 32;        // queries per wave
+constexpr int BQG = BW * BQ;  // queries per workgroup
+constexpr int BK = 64;        // keys per step
+constexpr int KR = 4;         // K ring slots
+constexpr int VR = 3;         // V staging ring slots
 
-__device__ __forceinline__ v8bf ld8(const uint16_t* p) {
-  uint4 u = *reinterpret_cast<const uint4*>(p);
-  return __builtin_bit_cast(v8bf, u);
+template <int D> struct BGeo {
+  static constexpr int NC = D / 16;          // 16-feature chunks of a score product
+  static constexpr int NO = D / 32;          // 32-feature blocks of the PV product
+  static constexpr int ROW = 2 * D;          // bytes of a K or V row
+  static constexpr int KSLOT = 2 * NC * 1024;  // K operands of a step: 2 key groups x NC chunks
+  static constexpr int VSLOT = BK * ROW;       // V rows of a step, row-major
+  static constexpr int VT = 4 * NO * 1024;     // V^T operands: 4 key chunks x NO blocks
+  static constexpr int K_OFF = 0;
+  static constexpr int VS_OFF = K_OFF + KR * KSLOT;
+  static constexpr int VT_OFF = VS_OFF + VR * VSLOT;
+  static constexpr int LDS = VT_OFF + 2 * VT;
+  // DMA per step: one 16-byte load per K operand region (2 NC), VSLOT/1024
+  // loads of V rows; waves 0-3 load K, waves 4-7 V, the same count each
+  static constexpr int NLOAD = 2 * NC;
+  static constexpr int PER_WAVE = NLOAD / 4;
+  static_assert(VSLOT / 1024 == NLOAD, "K and V sides issue the same number of loads");
+};
+
+// key (0..31 of a key group) fed to row r of the K operand: accumulator row
+// 8i + 4h + j then holds key 16(i/2) + 8h + 4(i%2) + j
+__device__ __forceinline__ constexpr int brow_key(int r) {
+  return 16 * ((r >> 3) >> 1) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+}
+
+// two floats -> packed bf16 (RNE)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const v2bf_b r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 template <int D>
-__global__ void __launch_bounds__(BNW * 64) bf16_fwd_kernel(const uint16_t* __restrict__ q,
-                                                             const uint16_t* __restrict__ k,
-                                                             const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
-                                                             int H, int Sq, int Skv, float c_log2) {
-  constexpr int KP = D + 8;     // padded K row (elements) in LDS
-  constexpr int VP = BKT + 8;   // padded V^T row (elements) in LDS
-  __shared__ __attribute__((aligned(16))) uint16_t ldsK[BKT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t ldsVt[D * VP];
+__global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v,
+                                                               uint16_t* __restrict__ out, int H, int Sq, int Skv,
+                                                               float c_log2) {
+  using G = BGeo<D>;
+  constexpr int NO = G::NO, NC = G::NC;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
   const int bh = blockIdx.y + blockIdx.z * H;
-  const int q0 = blockIdx.x * (BNW * BQW) + w * BQW;
-  const uint16_t* kb = k + (size_t)bh * Skv * D;
-  const uint16_t* vb = v + (size_t)bh * Skv * D;
+  const int qw0 = blockIdx.x * BQG + w * BQ;
+  const int ns = (Skv + BK - 1) / BK;
+  const int nklast = Skv - (ns - 1) * BK;
 
-  // Q^T operands (B of S^T): lane (n, g), chunk c: Q[q0+n][32c + 8g .. +8]
-  const int qrow = min(q0 + n, Sq - 1);
-  v8bf qB[D / 32];
+  // ---- DMA plan: wave w issues loads 4 (w & 3) .. 4 (w & 3) + PER_WAVE - 1 of
+  // its side every step, at constant per-lane offsets
+  const bool kside = w < 4;
+  int lofs[G::PER_WAVE], vofs[G::PER_WAVE];
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) qB[c] = ld8(q + ((size_t)bh * Sq + qrow) * D + 32 * c + 8 * g);
+  for (int j = 0; j < G::PER_WAVE; ++j) {
+    const int L = G::PER_WAVE * (w & 3) + j;
+    if (kside) {
+      // K operand region L: key group L / NC, feature chunk L % NC
+      const int kg = L / NC, c = L % NC;
+      lofs[j] = __builtin_amdgcn_readfirstlane(G::K_OFF + L * 1024);
+      vofs[j] = (32 * kg + brow_key(n)) * G::ROW + 32 * c + 16 * hh;
+    } else {
+      // V rows: load L covers 1024 bytes of the row-major step
+      lofs[j] = __builtin_amdgcn_readfirstlane(G::VS_OFF + L * 1024);
+      vofs[j] = L * 1024 + 16 * lane;
+    }
+  }
+  const uint64_t base = (uint64_t)(uintptr_t)((kside ? k : v) + (size_t)bh * Skv * D);
+  int rem = Skv * G::ROW;
+  const int stride = BK * G::ROW;
+  v4i rc = rsrc(base, rem);
+  auto advance = [&]() {
+    uint64_t b = ((uint64_t)(uint32_t)rc[1] << 32) | (uint32_t)rc[0];
+    b += (uint64_t)stride;
+    rc[0] = (int)(uint32_t)b;
+    rc[1] = (int)(uint32_t)(b >> 32);
+    rem -= stride;
+    rc[2] = rem > 0 ? rem : 0;
+  };
+  const uint32_t lds0 = lds_addr(smem);
+  int snext = 0;  // next step to fetch
+  int kfill = 0, vfill = 0;  // its K and V ring slots
+  auto issue = [&]() {
+    const uint32_t slot = lds0 + (uint32_t)(kside ? kfill * G::KSLOT : vfill * G::VSLOT);
+    const uint32_t keep = m0_save();
+#pragma unroll
+    for (int j = 0; j < G::PER_WAVE; ++j) dma_x4(rc, slot, (uint32_t)lofs[j], vofs[j]);
+    m0_restore(keep);
+    advance();
+    ++snext;
+    kfill = kfill == KR - 1 ? 0 : kfill + 1;
+    vfill = vfill == VR - 1 ? 0 : vfill + 1;
+  };
 
-  v4f_b O[D / 16];
+  // ---- transpose of one step's V rows (staging slot vs) into V^T operands
+  // (buffer vt): thread item (key quad kq, feature quad dq)
+  auto transpose = [&](int vs, int vt) {
+    const uint8_t* st = smem + G::VS_OFF + vs * G::VSLOT;
+    uint8_t* dst = smem + G::VT_OFF + vt * G::VT;
+    constexpr int ITEMS = 16 * (D / 4);
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) O[i] = v4f_b{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // running max (scaled, log2 units) of query n
-  float lpart = 0.0f;   // this lane's partial row sum
-
-  const int ntiles = (Skv + BKT - 1) / BKT;
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BKT;
-    const int nk = min(BKT, Skv - k0);
-    __syncthreads();
-    // stage K rows (zero beyond nk) and V transposed
-    for (int i = tid; i < BKT * D / 8; i += BNW * 64) {
-      const int key = i / (D / 8), c8 = i - key * (D / 8);
-      uint4 u = make_uint4(0, 0, 0, 0);
-      uint4 uv = make_uint4(0, 0, 0, 0);
-      if (key < nk) {
-        u = *reinterpret_cast<const uint4*>(kb + (size_t)(k0 + key) * D + 8 * c8);
-        uv = *reinterpret_cast<const uint4*>(vb + (size_t)(k0 + key) * D + 8 * c8);
-      }
-      *reinterpret_cast<uint4*>(ldsK + key * KP + 8 * c8) = u;
-      const uint32_t vv[4] = {uv.x, uv.y, uv.z, uv.w};
+    for (int it = tid; it < ITEMS; it += BW * 64) {
+      const int kq = it / (D / 4), dq = it % (D / 4);
+      uint2 r[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ldsVt[(8 * c8 + 2 * e) * VP + key] = (uint16_t)(vv[e] & 0xFFFFu);
-        ldsVt[(8 * c8 + 2 * e + 1) * VP + key] = (uint16_t)(vv[e] >> 16);
+      for (int e = 0; e < 4; ++e) r[e] = *reinterpret_cast<const uint2*>(st + (4 * kq + e) * G::ROW + 8 * dq);
+      // key k = 4 kq + e, feature d = 4 dq + f: chunk t = kq / 4, lane half
+      // (kq % 4) / 2, element 4 (kq % 2) + e of lane (h, d % 32)
+      const int t = kq >> 2, h2 = (kq >> 1) & 1;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int d = 4 * dq + f;
+        const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of (b, a)
+        const uint32_t w0 = (f < 2) ? r[0].x : r[0].y, w1 = (f < 2) ? r[1].x : r[1].y;
+        const uint32_t w2 = (f < 2) ? r[2].x : r[2].y, w3 = (f < 2) ? r[3].x : r[3].y;
+        const uint2 o2 = make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
+        const int region = t * NO + (d >> 5);
+        *reinterpret_cast<uint2*>(dst + region * 1024 + (32 * h2 + (d & 31)) * 16 + 8 * (kq & 1)) = o2;
       }
     }
-    __syncthreads();
+  };
 
-    // S^T blocks j = 0..3 (16 keys each); block j, A row r -> key 32(j/2) + 8(r/4) + 4(j%2) + r%4
-    v4f_b s[4];
+  // ---- Q^T operands (B of S^T): lane (q, h), chunk c: Q[q][16c + 8h .. +8]
+  v8bf qB[NC];
+  {
+    const int qrow = min(qw0 + n, Sq - 1);
+    const uint16_t* qp = q + ((size_t)bh * Sq + qrow) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qB[c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qp + 16 * c + 8 * hh));
+  }
+
+  v16f O[NO];
+#pragma unroll
+  for (int o = 0; o < NO; ++o)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) O[o][e] = 0.0f;
+  float m = -INFINITY;  // running max of query n (scaled, log2 units), lanes n and n + 32 agree
+  float lsum = 0.0f;    // this lane's share of the row sum
+
+  // prologue: steps 0..2 in flight; step 0 transposed before the loop
+  for (int s = 0; s < 3; ++s) issue();
+  wait_vm<2 * G::PER_WAVE>();
+  barrier();
+  transpose(0, 0);
+  int kread = 0, vstage = 1;  // K ring slot of step u; staging slot of step u + 1
+
+  for (int u = 0; u < ns; ++u) {
+    // steps <= u + 1 landed; after the barrier the loads of step u + 3 reuse
+    // the K slot of step u - 1 and the staging slot of step u, both consumed
+    wait_vm<G::PER_WAVE>();
+    wait_lgkm0();  // the previous step's transpose writes (ds_write) are done
+    barrier();
+    issue();
+    transpose(vstage, (u + 1) & 1);
+
+    // ---- S^T = K Q^T for the step's two key groups
+    const uint8_t* ks = smem + G::K_OFF + kread * G::KSLOT;
+    v16f S[2];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(ks + (kg * NC + c) * 1024 + 16 * lane));
+        if (c == 0) {
+          v16f z;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+          S[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[0], z, 0, 0, 0);
+        } else {
+          S[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[c], S[kg], 0, 0, 0);
+        }
+      }
+    }
+    // lane (q, h), register 4i + j of key group kg holds key 32 kg + 16(i/2) + 8h + 4(i%2) + j
+    if (u == ns - 1 && nklast < BK) {
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int i = e >> 2, j = e & 3;
+          const int key = 32 * kg + 16 * (i >> 1) + 8 * hh + 4 * (i & 1) + j;
+          if (key >= nklast) S[kg][e] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kg][e]);
+    mx *= c_log2;
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = __builtin_fmaxf(m, mx);
+    if (__ballot(mnew > m) != 0) {
+      // the reference grows: rescale O and l by exp2(m_old - m_new)
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      lsum *= alpha;
+      int base4 = hh << 4;  // byte address of lane 4h
+      asm volatile("" : "+v"(base4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float r = __int_as_float(__builtin_amdgcn_ds_bpermute(base4 + 4 * (8 * i + j), __float_as_int(alpha)));
+#pragma unroll
+          for (int o = 0; o < NO; ++o) O[o][4 * i + j] *= r;
+        }
+      m = mnew;
+    }
+    // p = exp2(s c - m), l += p, P operands of the four 16-key chunks
+    uint32_t pw[16];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kg][e], c_log2, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kg][e + 1], c_log2, -m));
+        lsum += p0 + p1;
+        pw[8 * kg + e / 2] = pk_bf16(p0, p1);
+      }
+    // ---- O += P V: chunk t = 2 kg + (i / 2) holds registers 8t .. 8t + 7
+    const uint8_t* vt = smem + G::VT_OFF + (u & 1) * G::VT;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v8bf pa = __builtin_bit_cast(v8bf, uint4{pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]});
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        const v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(vt + (t * NO + o) * 1024 + 16 * lane));
+        O[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, b, O[o], 0, 0, 0);
+      }
+    }
+    kread = kread == KR - 1 ? 0 : kread + 1;
+    vstage = vstage == VR - 1 ? 0 : vstage + 1;
+  }
+  wait_vm<0>();  // loads past the end are still in flight
+
+  // ---- O / l -> bf16: lane (d % 32, h) register 4i + j holds query 8i + 4h + j
+  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = lane & 15;
-      const int key = 32 * (j >> 1) + 8 * (r >> 2) + 4 * (j & 1) + (r & 3);
-      v4f_b acc = {0.f, 0.f, 0.f, 0.f};
+      const int qi = 8 * i + 4 * hh + j;
+      const float lq = __shfl(ltot, qi, 64);
+      const int qq = qw0 + qi;
+      if (qq < Sq) {
+        const float inv = 1.0f / lq;
+        uint16_t* orow = out + ((size_t)bh * Sq + qq) * D;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        v8bf a = ld8(ldsK + key * KP + 32 * c + 8 * g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[c], acc, 0, 0, 0);
-      }
-      s[j] = acc;
-    }
-    // lane (n, g) now holds query n, keys 32(j/2) + 8g + 4(j%2) + r'
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 32 * (j >> 1) + 8 * g + 4 * (j & 1) + r;
-        float x = (key < nk) ? s[j][r] * c_log2 : -INFINITY;
-        s[j][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(m, tmax);
-    const float alpha = exp2f(m - mnew);  // m = -inf on the first tile -> 0
-    m = mnew;
-    float psum = 0.0f;
-    v8bf pA[2];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[2 * cc + h][r] - mnew);
-          psum += p;
-          pA[cc][4 * h + r] = (__bf16)p;
+        for (int o = 0; o < NO; ++o) {
+          uint32_t uo = __float_as_uint(O[o][4 * i + j] * inv);
+          uo = (uo + 0x7FFFu + ((uo >> 16) & 1u)) >> 16;  // RNE to bf16 (finite values)
+          orow[32 * o + n] = (uint16_t)uo;
         }
-    lpart = lpart * alpha + psum;
-    // rescale O rows (queries 4g + r): alpha of query q lives in lanes with n = q
-    float ar[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r, 64);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[i][r] *= ar[r];
-    // O += P V: chunk cc, d block i: B lane (n, g) = V^T[16i + n][32cc + 8g .. +8]
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i) {
-        v8bf b = ld8(ldsVt + (16 * i + n) * VP + 32 * cc + 8 * g);
-        O[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pA[cc], b, O[i], 0, 0, 0);
-      }
-  }
-  // l of query n = sum over the 4 lanes of the query
-  float l = lpart + __shfl_xor(lpart, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int qq = q0 + 4 * g + r;
-    const float lq = __shfl(l, 4 * g + r, 64);
-    if (qq < Sq) {
-      const float inv = 1.0f / lq;
-      uint16_t* orow = out + ((size_t)bh * Sq + qq) * D;
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i) {
-        __bf16 b = (__bf16)(O[i][r] * inv);
-        orow[16 * i + n] = __builtin_bit_cast(uint16_t, b);
       }
     }
-  }
 }
+
+}  // namespace
 
 hipError_t launch_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int B, int H,
                            int Sq, int Skv, int D, float softmax_scale, hipStream_t stream) {
   const float c_log2 = softmax_scale * 1.4426950408889634f;
-  dim3 grid((unsigned)((Sq + BNW * BQW - 1) / (BNW * BQW)), (unsigned)H, (unsigned)B);
+  dim3 grid((unsigned)((Sq + BQG - 1) / BQG), (unsigned)H, (unsigned)B);
   if (D == 128)
-    hipLaunchKernelGGL(bf16_fwd_kernel<128>, grid, dim3(BNW * 64), 0, stream, q, k, v, out, H, Sq, Skv, c_log2);
+    hipLaunchKernelGGL(bf16_fwd_kernel<128>, grid, dim3(BW * 64), 0, stream, q, k, v, out, H, Sq, Skv, c_log2);
   else
-    hipLaunchKernelGGL(bf16_fwd_kernel<64>, grid, dim3(BNW * 64), 0, stream, q, k, v, out, H, Sq, Skv, c_log2);
+    hipLaunchKernelGGL(bf16_fwd_kernel<64>, grid, dim3(BW * 64), 0, stream, q, k, v, out, H, Sq, Skv, c_log2);
   return hipGetLastError();
 }
 

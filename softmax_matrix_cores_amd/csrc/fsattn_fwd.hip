@@ -15,12 +15,12 @@
 //
 // Mapping to CDNA4:
 //   * 8 waves per workgroup (two per SIMD), 32 queries per wave.  Keys advance
-//     in steps of 64 with one workgroup barrier per step.  The two waves of a
-//     SIMD run the step in opposite phase ("ping-pong"): waves 0-3 issue the
-//     score and PV products of a step and then convert the scores on the
-//     VALU; waves 4-7 first convert the previous step's scores and then issue
-//     their products.  Between two barriers one wave of each SIMD keeps the
-//     matrix core busy while the other works on the VALU.
+//     in steps of 64 with one workgroup barrier per step.  Every wave runs the
+//     same schedule: after the barrier it reads the K operands of step u+1,
+//     issues the PV products of step u-1 interleaved with the VALU conversion
+//     of step u, reads the V operands of step u and issues the score products
+//     of step u+1, so that every LDS read has a phase of the step to arrive
+//     and the matrix core works while the VALU converts.
 //   * every product is v_mfma_scale_f32_32x32x64_f8f6f4: S^T = K Q^T (2 key
 //     groups x D/64 feature halves, the fold offset C_i as the accumulator's
 //     initial value), O += P V (D/32 feature blocks).  l += P 1 uses one
@@ -60,6 +60,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "lds_dma.h"
 #include "mx_device.h"
 
 namespace fsattn {
@@ -71,7 +72,6 @@ constexpr int QWG = NW * QW;  // queries per workgroup
 constexpr int KS = 64;        // keys per step
 constexpr int NS = 8;         // LDS ring slots
 constexpr int PF = NS - 2;    // steps fetched ahead
-constexpr int RSRC_W3 = 0x00020000;
 
 template <int F> struct Opd {
   static constexpr int bits = Fmt<F>::bits;
@@ -125,50 +125,6 @@ template <> struct PFlush<E2M3> { static constexpr float t = 896.0f; };
 template <> struct PFlush<E4M3> { static constexpr float t = 2432.0f; };
 
 __device__ __forceinline__ float wshfl(float v, int src) { return __shfl(v, src, 64); }
-
-template <int N> __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-// workgroup barrier without the memory fence of __syncthreads (which would
-// wait for every outstanding DMA); the clobber keeps LDS reads below it
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Buffer descriptor (raw, stride 0) of `bytes` bytes at `base`, in SGPRs.
-// Reads at or beyond `bytes` return zeros.
-__device__ __forceinline__ v4i rsrc(uint64_t b, int bytes) {
-  const int nrec = bytes < 0 ? 0 : bytes;
-  return v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)b), (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu),
-             __builtin_amdgcn_readfirstlane(nrec), RSRC_W3};
-}
-
-// buffer_load ... lds: each lane's 16 (or 4) bytes at voff land in LDS at
-// M0 + 16 (or 4) * lane.  Issued as inline asm so that the compiler does not
-// treat the asynchronous LDS write as aliasing every later LDS read (it would
-// wait for all outstanding loads before each one); completion is tracked
-// explicitly with s_waitcnt vmcnt and published with s_barrier.  A group of
-// loads is bracketed by m0_save / m0_restore (M0 is the LDS destination).
-__device__ __forceinline__ uint32_t m0_save() {
-  uint32_t k;
-  asm volatile("s_mov_b32 %0, m0" : "=s"(k));
-  return k;
-}
-__device__ __forceinline__ void m0_restore(uint32_t k) { asm volatile("s_mov_b32 m0, %0" ::"s"(k)); }
-__device__ __forceinline__ void dma_x4(const v4i& rs, uint32_t slot, uint32_t off, int voff) {
-  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds" ::"s"(slot), "s"(off), "v"(voff),
-               "s"(rs)
-               : "scc");
-}
-__device__ __forceinline__ void dma_x1(const v4i& rs, uint32_t slot, uint32_t off, int voff) {
-  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds" ::"s"(slot), "s"(off), "v"(voff),
-               "s"(rs)
-               : "scc");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
 
 // One lane's MFMA operand from an LDS region in operand order
 template <int F> __device__ __forceinline__ v8i lds_operand(const uint8_t* region, int lane) {
