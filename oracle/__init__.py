@@ -50,6 +50,10 @@ class Params(ctypes.Structure):
     ]
 
 
+class Mask(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int), ("q_lens", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -73,6 +77,8 @@ def lib():
         L.fso_stage1.restype = ctypes.c_uint16
         L.fso_stage1.argtypes = [ctypes.c_float]
         L.fso_forward.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P, ctypes.c_int64, P, P, P, P, P]
+        L.fso_forward_masked.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Mask), P, P, P, P, P, P, P,
+                                         ctypes.c_int64, P, P, P, P, P]
         L.fso_reference.argtypes = [ctypes.POINTER(Params), ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int64, P]
         L.fso_reference_bf16.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double, P, P, P, P, ctypes.c_int64,
                                                               ctypes.c_int, P]
@@ -149,8 +155,9 @@ def make_params(B, H, Sq, Skv, D, qk_elem, v_elem, p_elem, tau=8.0, c=0.0, kv_ti
                   exp_mode, p_mode, fold_mode, nthreads)
 
 
-def forward(p: Params, q, k, v, rows=None, want_p=False):
-    """q, k, v: (codes, scales) tuples in the quantizer layout.  Returns dict."""
+def forward(p: Params, q, k, v, rows=None, want_p=False, causal=False, q_lens=None, kv_lens=None):
+    """q, k, v: (codes, scales) tuples in the quantizer layout.  Returns dict.
+    causal / q_lens / kv_lens: the mask of fso_forward_masked (lens: [B] ints)."""
     nrows = p.B * p.H * p.Sq if rows is None else len(rows)
     rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     O = np.zeros((nrows, p.D), np.float64)
@@ -160,8 +167,18 @@ def forward(p: Params, q, k, v, rows=None, want_p=False):
     pc = np.zeros((nrows, s32), np.uint8) if want_p else None
     ps = np.zeros((nrows, s32 // 32), np.uint8) if want_p else None
     args = [np.ascontiguousarray(a) for a in (q[0], q[1], k[0], k[1], v[0], v[1])]
-    rc = lib().fso_forward(ctypes.byref(p), *[_ptr(a) for a in args], _ptr(rows_a), nrows, _ptr(O), _ptr(L),
-                           _ptr(cnt), _ptr(pc), _ptr(ps))
+    if causal or q_lens is not None or kv_lens is not None:
+        ql = None if q_lens is None else np.ascontiguousarray(q_lens, dtype=np.int32)
+        kl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
+        for a in (ql, kl):
+            if a is not None and a.shape != (p.B,):
+                raise ValueError("q_lens / kv_lens must have B entries")
+        m = Mask(1 if causal else 0, _ptr(ql), _ptr(kl))
+        rc = lib().fso_forward_masked(ctypes.byref(p), ctypes.byref(m), *[_ptr(a) for a in args], _ptr(rows_a),
+                                      nrows, _ptr(O), _ptr(L), _ptr(cnt), _ptr(pc), _ptr(ps))
+    else:
+        rc = lib().fso_forward(ctypes.byref(p), *[_ptr(a) for a in args], _ptr(rows_a), nrows, _ptr(O), _ptr(L),
+                               _ptr(cnt), _ptr(pc), _ptr(ps))
     if rc != 0:
         raise ValueError(f"fso_forward failed ({rc})")
     out = {"O": O, "l": L, "counts": cnt}

@@ -493,6 +493,7 @@ uint16_t fso_stage1(float t) {
 
 typedef struct {
   const fso_params* p;
+  const fso_mask* mask; /* NULL: no mask */
   int ref; /* 0 = fused forward, else FSO_REF_* */
   const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
   const int64_t* rows;
@@ -557,12 +558,28 @@ typedef struct {
   uint8_t* psc;    /* [S32/32] */
 } rowbuf_t;
 
+static int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/* last key row `row` may see (-1: none), from the mask (fso_mask) */
+static int64_t last_visible_key(const fso_params* p, const fso_mask* m, int64_t row) {
+  int64_t head = row / p->Sq, b = head / p->H, i = row % p->Sq;
+  int64_t qlen = p->Sq, kvlen = p->Skv;
+  if (m && m->q_lens) qlen = clamp64(m->q_lens[b], 0, p->Sq);
+  if (m && m->kv_lens) kvlen = clamp64(m->kv_lens[b], 0, p->Skv);
+  if (i >= qlen) return -1;
+  int64_t lim = kvlen - 1;
+  if (m && m->causal && i + kvlen - qlen < lim) lim = i + kvlen - qlen;
+  return lim < -1 ? -1 : lim;
+}
+
 static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
   const fso_params* p = J->p;
   int D = p->D, nbd = D / 32;
-  int64_t Skv = p->Skv, S32 = skv32_of(p);
+  int64_t S32 = skv32_of(p);
   int64_t row = J->rows ? J->rows[ri] : ri;
   int64_t head = row / p->Sq;
+  /* keys [0, Skv) are visible: a masked row sees a prefix of the keys */
+  int64_t Skv = last_visible_key(p, J->mask, row) + 1;
   int qbb = fso_block_bytes(p->qk_elem);
   int bad;
   decode_row(p->qk_elem, J->qc + (row * nbd) * qbb, J->qs + row * nbd, D, rb->qm, rb->qe, &bad);
@@ -570,6 +587,16 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
   for (int d = 0; d < D; ++d) O[d] = 0.0;
   double l = 0.0;
   int32_t cnt = 0;
+  memset(rb->pc, 0, (size_t)S32);
+  memset(rb->psc, 0, (size_t)(S32 / 32));
+  if (Skv == 0) {
+    /* no visible key: O = 0, l = 0 */
+    if (J->L) J->L[ri] = 0.0;
+    if (J->counts) J->counts[ri] = 0;
+    if (J->pcodes) memset(J->pcodes + ri * S32, 0, (size_t)S32);
+    if (J->pscales) memset(J->pscales + ri * (S32 / 32), 0, (size_t)(S32 / 32));
+    return;
+  }
   const int exact = (p->fold_mode == FSO_FOLD_EXACT);
   /* T0 = 128*127 - c maps the reference to 2^0; T_gate = T0 + 128*tau (R1, R6) */
   double T0 = exact ? (128.0 * 127.0 - p->c) : (double)(float)(128.0 * 127.0 - p->c);
@@ -622,8 +649,10 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
       l *= rho;
       ++cnt;
     }
-    /* stage 1: folded score -> BF16 pattern (or the exact exponential) */
-    int64_t kb0 = k0, kb1 = (j == ntiles - 1) ? S32 : k0 + bc;
+    /* stage 1: folded score -> BF16 pattern (or the exact exponential); the
+     * P blocks of the tile run to its end (to S32 on the last tile of the
+     * keys), absent keys giving 0 */
+    int64_t kb0 = k0, kb1 = k0 + bc < S32 ? k0 + bc : S32;
     for (int64_t k = kb0; k < kb1; ++k) {
       double v = 0.0;
       if (k < Skv) {
@@ -766,9 +795,10 @@ static int check_params(const fso_params* p) {
   return 1;
 }
 
-static int run_rows(const fso_params* p, int ref, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
-                    const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int64_t* rows, int64_t nrows,
-                    double* out_O, double* out_l, int32_t* counts, uint8_t* pcodes, uint8_t* pscales) {
+static int run_rows(const fso_params* p, const fso_mask* mask, int ref, const uint8_t* qc, const uint8_t* qs,
+                    const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int64_t* rows,
+                    int64_t nrows, double* out_O, double* out_l, int32_t* counts, uint8_t* pcodes,
+                    uint8_t* pscales) {
   if (!check_params(p)) return FSO_EINVAL;
   int64_t total = (int64_t)p->B * p->H * p->Sq;
   if (!rows) nrows = total;
@@ -779,7 +809,7 @@ static int run_rows(const fso_params* p, int ref, const uint8_t* qc, const uint8
   int64_t Skv = p->Skv, S32 = skv32_of(p);
   job_t J;
   memset(&J, 0, sizeof J);
-  J.p = p; J.ref = ref; J.qc = qc; J.qs = qs; J.kc = kc; J.ks = ks; J.vc = vc; J.vs = vs;
+  J.p = p; J.mask = mask; J.ref = ref; J.qc = qc; J.qs = qs; J.kc = kc; J.ks = ks; J.vc = vc; J.vs = vs;
   J.rows = rows; J.nrows = nrows; J.O = out_O; J.L = out_l; J.counts = counts; J.pcodes = pcodes; J.pscales = pscales;
   J.kmint = (int64_t*)malloc(sizeof(int64_t) * (size_t)(Skv * D));
   J.kbexp = (int*)malloc(sizeof(int) * (size_t)(Skv * (D / 32)));
@@ -818,14 +848,21 @@ static int run_rows(const fso_params* p, int ref, const uint8_t* qc, const uint8
 int fso_forward(const fso_params* p, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                 const uint8_t* vc, const uint8_t* vs, const int64_t* rows, int64_t nrows, double* out_O,
                 double* out_l, int32_t* counts, uint8_t* p_codes, uint8_t* p_scales) {
-  return run_rows(p, 0, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, out_l, counts, p_codes, p_scales);
+  return run_rows(p, NULL, 0, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, out_l, counts, p_codes, p_scales);
+}
+
+int fso_forward_masked(const fso_params* p, const fso_mask* m, const uint8_t* qc, const uint8_t* qs,
+                       const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs,
+                       const int64_t* rows, int64_t nrows, double* out_O, double* out_l, int32_t* counts,
+                       uint8_t* p_codes, uint8_t* p_scales) {
+  return run_rows(p, m, 0, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, out_l, counts, p_codes, p_scales);
 }
 
 int fso_reference(const fso_params* p, int ref, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                   const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int64_t* rows, int64_t nrows,
                   double* out_O) {
   if (ref < FSO_REF_R1 || ref > FSO_REF_R3) return FSO_EINVAL;
-  return run_rows(p, ref, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, NULL, NULL, NULL, NULL);
+  return run_rows(p, NULL, ref, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, NULL, NULL, NULL, NULL);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -123,6 +123,32 @@ int fso_forward(const fso_params* p,
                 double* out_O, double* out_l, int32_t* counts,
                 uint8_t* p_codes, uint8_t* p_scales);
 
+/*
+ * Masked and variable-length attention (the pages put masks before the
+ * score shift and probability generation: "Fused softmax makes quantized
+ * attention faster on AMD GPUs", section "What the evidence shows").
+ *  causal   query i of batch b sees key k only if k <= i + kv_len_b - q_len_b
+ *           (queries aligned to the end of the keys)
+ *  q_lens   optional host [B]: valid queries per batch, clamped to [0, Sq]
+ *  kv_lens  optional host [B]: valid keys per batch, clamped to [0, Skv]
+ * A masked key is absent: it takes no part in a tile's maximum (reference or
+ * gate) and its P is 0.  Tiles keep their positions (tile j = keys
+ * [j*kv_tile, (j+1)*kv_tile)).  A row with no visible key, and every row
+ * i >= q_len_b, has O = 0, l = 0 and count 0.
+ */
+typedef struct {
+  int causal;
+  const int32_t* q_lens;
+  const int32_t* kv_lens;
+} fso_mask;
+
+int fso_forward_masked(const fso_params* p, const fso_mask* m,
+                       const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                       const uint8_t* vc, const uint8_t* vs,
+                       const int64_t* rows, int64_t nrows,
+                       double* out_O, double* out_l, int32_t* counts,
+                       uint8_t* p_codes, uint8_t* p_scales);
+
 /* References on the same quantized operands (see FSO_REF_*). */
 int fso_reference(const fso_params* p, int ref,
                   const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,

@@ -134,8 +134,11 @@ def bf16_bits_to_fraction(u16: np.ndarray) -> list[Fraction]:
 
 
 def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, tau: float = 8.0,
-            kv_tile: int = 64, c: float = 0.0):
+            kv_tile: int = 64, c: float = 0.0, visible=None):
     """Tiny forward for one head.  qb [Sq,D], kb/vb [Skv,D] uint16 bf16 bit patterns.
+    visible: optional [Sq] number of keys row i sees (keys 0 .. visible[i]-1);
+    the others are absent (no part in any maximum, P = 0); a row that sees no
+    key gives O = 0.
     Returns (O [Sq,D] float, counts [Sq], P codes [Sq,Skv32], P scales [Sq,Skv32/32])."""
     Sq, D = qb.shape
     Skv = kb.shape[0]
@@ -171,14 +174,17 @@ def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, ta
     counts = np.zeros(Sq, np.int32)
     pcodes = np.zeros((Sq, S32), np.int64)
     pscales = np.zeros((Sq, S32 // 32), np.int64)
-    ntiles = (Skv + kv_tile - 1) // kv_tile
     for i in range(Sq):
-        sig = [sum(a * b for a, b in zip(Qh[i], Kh[k])) for k in range(Skv)]
+        n_i = Skv if visible is None else max(0, min(Skv, int(visible[i])))
+        if n_i == 0:
+            continue
+        ntiles = (n_i + kv_tile - 1) // kv_tile
+        sig = [sum(a * b for a, b in zip(Qh[i], Kh[k])) for k in range(n_i)]
         num = [Fraction(0)] * D
         den = Fraction(0)
         C = Fraction(0)
         for j in range(ntiles):
-            ks = list(range(j * kv_tile, min((j + 1) * kv_tile, Skv)))
+            ks = list(range(j * kv_tile, min((j + 1) * kv_tile, n_i)))
             if j == 0:
                 t = {k: fl32(sig[k]) for k in ks}
                 C = fl32(T0 - max(t.values()))
@@ -195,10 +201,10 @@ def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, ta
                     den = den * Fraction(rho)
                     counts[i] += 1
             # stage 1 (integer part of the folded score as a BF16 pattern) and stage 2 (MX)
-            hi = S32 if j == ntiles - 1 else (j + 1) * kv_tile
+            hi = min((j + 1) * kv_tile, S32)
             pvals = {}
             for k in range(j * kv_tile, hi):
-                if k < Skv and t[k] >= 128:
+                if k < n_i and t[k] >= 128:
                     pvals[k] = bf16_value(min(math.floor(t[k]), 0x7F7F))
                 else:
                     pvals[k] = Fraction(0)
