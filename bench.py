@@ -13,6 +13,8 @@ Inputs are resident in HBM before timing starts.  Reported:
                in-library BF16 attention kernel for each format of the workload
   cpu_baseline the CPU oracle on a bounded sample of query rows of the same
                workload, in the same unit
+  causal       (video workloads) the fused kernel under a causal mask on the
+               same inputs: 4*B*H*D*S(S+1)/2 flops (visible pairs only)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video-mxfp6]
 """
@@ -101,6 +103,34 @@ def time_path(fs, W, w, q, k, v, steps, warmup):
     return total / steps, sum(fwd) / len(fwd), max(fwd), sum(qnt) / len(qnt), out, counts
 
 
+def time_fused_causal(fs, w, q, k, v, steps, warmup):
+    """Mean fused-kernel time (ms) under a causal mask, HIP events on the launch stream."""
+    import torch
+
+    st = torch.cuda.current_stream()
+    Q = fs.quantize_mx(q, 0, w.qk_elem, prescale=fs.fold_prescale(w.sigma))
+    K = fs.quantize_mx(k, 0, w.qk_elem)
+    V = fs.quantize_mx(v, 1, w.v_elem)
+    out = torch.empty(w.B, w.H, w.Sq, w.D, dtype=torch.bfloat16, device=q.device)
+    counts = torch.zeros(w.B, w.H, w.Sq, dtype=torch.int32, device=q.device)
+
+    def run():
+        fs.forward(Q, K, V, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=w.tau, kv_tile=w.kv_tile,
+                   counts=counts, out=out, causal=True)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(st)
+        run()
+        b.record(st)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in ev]
+    return sum(ts) / len(ts), int(counts.sum().item())
+
+
 def time_bf16(fs, w, q, k, v, steps, warmup):
     import torch
 
@@ -165,6 +195,7 @@ def main():
     ap.add_argument("--also", default="auto", help="other formats of the same shape (auto: the video pair)")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-causal", action="store_true", help="skip the causal-mask leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration for profiles)")
@@ -224,6 +255,16 @@ def main():
         formats[vw.name] = rec
         if vw is w:
             main_res = (st_ms, fwd_ms, rec)
+
+    if not args.no_causal and w.name.startswith("video-") and w.Sq == w.Skv:
+        print(f"[bench] fused {w.name} causal", file=sys.stderr, flush=True)
+        c_ms, c_cnt = time_fused_causal(fs, w, q, k, v, max(3, args.steps // 2), 1)
+        c_flops = 4 * w.B * w.H * w.D * (w.Sq * (w.Sq + 1) // 2)
+        c_tf = c_flops / (c_ms * 1e-3) / 1e12
+        formats[w.name + "-causal"] = {"kernel_tflops": round(c_tf, 2), "kernel_ms": round(c_ms, 4),
+                                       "mx_mfma_util": round(c_tf / _peak_for(w), 4), "rollbacks": c_cnt,
+                                       "flops": c_flops,
+                                       "time_vs_unmasked": round(c_ms / main_res[1], 4)}
 
     st_ms, fwd_ms, rec = main_res
     value = w.flops / (st_ms * 1e-3) / 1e12

@@ -164,6 +164,38 @@ int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsat
                    const fsattn_mx_tensor* v, void* out, void* stream);
 
 /*
+ * fsattn_forward_masked -- fsattn_forward with causal and variable-length
+ * masks.  The pages apply masks before the score shift and probability
+ * generation ("Fused softmax makes quantized attention faster on AMD GPUs",
+ * chiosa.app, section "What the evidence shows"): a masked key takes no part
+ * in any tile maximum (tile-0 reference, rollback gate) and its P is 0.
+ * Tiles keep their positions (tile j = keys [j*kv_tile, (j+1)*kv_tile)).
+ *
+ * mask (may be NULL = no mask, the same as fsattn_forward):
+ *   causal   0 or 1.  1: query i of batch b sees key k only if
+ *            k <= i + kv_len_b - q_len_b (queries aligned to the end of the
+ *            keys, as for a query block appended to a key cache).
+ *   q_lens   optional DEVICE int32 [B]: valid queries of each batch (rows
+ *            i >= q_len_b are stored as 0 with count 0); NULL = Sq.
+ *   kv_lens  optional DEVICE int32 [B]: valid keys of each batch; NULL = Skv.
+ *   Lengths are clamped to [0, Sq] / [0, Skv] on the device.  A row that sees
+ *   no key is stored as 0 with count 0.  Keys past kv_len_b must still hold
+ *   quantizer output (finite codes): they are read and multiplied by P = 0.
+ * Everything else (layouts, params, errors) is as for fsattn_forward; in
+ * addition FSATTN_E_INVALID_ARG if causal is not 0/1 and FSATTN_E_ALIGNMENT
+ * if q_lens or kv_lens is not 4-byte aligned.  The P dump (params) leaves
+ * rows past q_len_b untouched.
+ */
+typedef struct {
+  int causal;
+  const int32_t* q_lens;
+  const int32_t* kv_lens;
+} fsattn_mask;
+
+int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
+                          const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream);
+
+/*
  * fsattn_forward_bf16_baseline -- conventional attention forward in BF16
  * (the baseline the pages compare against, paragraph 8): tiled online
  * softmax with a running max and rescaling ("Conventional implementations

@@ -26,7 +26,7 @@ SCALE_FITMAX, SCALE_OCP_FLOOR = 0, 1
 # every symbol include/fsattn.h declares
 ABI_SYMBOLS = (
     "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
-    "fsattn_quantize_mx", "fsattn_forward", "fsattn_forward_bf16_baseline",
+    "fsattn_quantize_mx", "fsattn_forward", "fsattn_forward_masked", "fsattn_forward_bf16_baseline",
 )
 
 
@@ -52,6 +52,10 @@ class _Params(ctypes.Structure):
     ]
 
 
+class _Mask(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int), ("q_lens", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -75,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.fsattn_forward.restype = I
         L.fsattn_forward.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
                                      ctypes.POINTER(_MxTensor), V, V]
+        L.fsattn_forward_masked.restype = I
+        L.fsattn_forward_masked.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_Mask),
+                                            ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
+                                            ctypes.POINTER(_MxTensor), V, V]
         L.fsattn_forward_bf16_baseline.restype = I
         L.fsattn_forward_bf16_baseline.argtypes = [V, V, V, I, I, I, I, I, ctypes.c_float, V, V]
         _lib = L
@@ -153,10 +161,12 @@ def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qk_elem, v_e
 
 def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv: int, D: int, softmax_scale: float,
             p_elem, tau: float = 8.0, c: float = 0.0, kv_tile: int = 64, counts: torch.Tensor | None = None,
-            out: torch.Tensor | None = None, p_dump: tuple | None = None, stream=None) -> torch.Tensor:
+            out: torch.Tensor | None = None, p_dump: tuple | None = None, stream=None, causal: bool = False,
+            q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None) -> torch.Tensor:
     """Fused-Softmax attention forward.  Returns bf16 [B,H,Sq,D].
     counts: optional int32 [B,H,Sq] written with rollback counts.
-    p_dump: optional (b, h, row0, row1, codes uint8 [rows, Skv32], scales uint8 [rows, Skv32/32])."""
+    p_dump: optional (b, h, row0, row1, codes uint8 [rows, Skv32], scales uint8 [rows, Skv32/32]).
+    causal / q_lens / kv_lens: masks (fsattn_forward_masked); lens are device int32 [B]."""
     dev = Q.codes.device
     if out is None:
         out = torch.empty(B, H, Sq, D, dtype=torch.bfloat16, device=dev)
@@ -167,6 +177,17 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
         p.p_dump_codes, p.p_dump_scales = pc.data_ptr(), ps.data_ptr()
         p.p_b, p.p_h, p.p_row0, p.p_row1 = b, h, r0, r1
     q, k, v = Q._c(), K._c(), V._c()
+    if causal or q_lens is not None or kv_lens is not None:
+        for t in (q_lens, kv_lens):
+            if t is not None and (t.dtype != torch.int32 or t.device != dev or t.shape != (B,) or
+                                  not t.is_contiguous()):
+                raise ValueError("q_lens / kv_lens must be contiguous int32 [B] on the operands' device")
+        m = _Mask(1 if causal else 0, q_lens.data_ptr() if q_lens is not None else None,
+                  kv_lens.data_ptr() if kv_lens is not None else None)
+        st = lib().fsattn_forward_masked(ctypes.byref(p), ctypes.byref(m), ctypes.byref(q), ctypes.byref(k),
+                                         ctypes.byref(v), out.data_ptr(), _stream(stream))
+        _check("fsattn_forward_masked", st)
+        return out
     st = lib().fsattn_forward(ctypes.byref(p), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out.data_ptr(),
                               _stream(stream))
     _check("fsattn_forward", st)

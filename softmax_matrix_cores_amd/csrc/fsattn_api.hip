@@ -95,9 +95,13 @@ int fsattn_quantize_mx(const void* src, int64_t n_mat, int64_t rows, int64_t col
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
 }
 
-int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsattn_mx_tensor* k,
-                   const fsattn_mx_tensor* v, void* out, void* stream) {
+int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
+                          const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream) {
   if (!p || !q || !k || !v) return FSATTN_E_INVALID_ARG;
+  if (mask) {
+    if (mask->causal != 0 && mask->causal != 1) return FSATTN_E_INVALID_ARG;
+    if (!aligned(mask->q_lens, 4) || !aligned(mask->kv_lens, 4)) return FSATTN_E_ALIGNMENT;
+  }
   if (p->B < 0 || p->H < 0 || p->Sq < 0 || p->Skv < 1) return FSATTN_E_INVALID_ARG;
   if (p->D != 64 && p->D != 128) return FSATTN_E_INVALID_ARG;
   if (p->kv_tile != 64 && p->kv_tile != 128) return FSATTN_E_INVALID_ARG;
@@ -145,9 +149,17 @@ int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsat
   a.Tg = (float)(128.0 * (127.0 + (double)p->tau) - (double)p->schraudolph_c);
   a.kv128 = p->kv_tile == 128;
   a.fitmax = 1;
+  a.causal = mask ? mask->causal : 0;
+  a.q_lens = mask ? mask->q_lens : nullptr;
+  a.kv_lens = mask ? mask->kv_lens : nullptr;
   hipError_t e = fsattn::launch_fsattn_fwd(a, p->B, p->D, q->elem, v->elem, p->p_elem,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
+}
+
+int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsattn_mx_tensor* k,
+                   const fsattn_mx_tensor* v, void* out, void* stream) {
+  return fsattn_forward_masked(p, nullptr, q, k, v, out, stream);
 }
 
 int fsattn_forward_bf16_baseline(const void* q, const void* k, const void* v, int B, int H, int Sq, int Skv, int D,

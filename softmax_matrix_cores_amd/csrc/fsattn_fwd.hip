@@ -309,9 +309,9 @@ __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, floa
 
 // optional P dump (debug): one code byte per key and the E8M0 per 32 keys
 template <int PE>
-__device__ __forceinline__ void dump_p(const FwdArgs& a, int bh, int qq, int k0, int hh, const v8i& pA,
+__device__ __forceinline__ void dump_p(const FwdArgs& a, int bh, int qq, int q_len, int k0, int hh, const v8i& pA,
                                        const uint32_t (&dsc)[2]) {
-  if (bh != a.pd_bh || qq < a.pd_row0 || qq >= a.pd_row1 || qq >= a.Sq) return;
+  if (bh != a.pd_bh || qq < a.pd_row0 || qq >= a.pd_row1 || qq >= q_len) return;
   const int nb32 = a.nb32;
   const size_t S32 = (size_t)nb32 * 32;
   uint8_t* drow = a.pd_codes + (size_t)(qq - a.pd_row0) * S32;
@@ -327,6 +327,33 @@ __device__ __forceinline__ void dump_p(const FwdArgs& a, int bh, int qq, int k0,
   }
   const int kb = k0 / 32 + hh;
   if (kb < nb32) srow[kb] = (uint8_t)(Opd<PE>::split ? dsc[hh] : dsc[0]);
+}
+
+// O / l of the wave's 32 queries to bf16 (RNE), and the rollback counts.
+// Rows past q_len, and rows with l = 0 (no visible key), are stored as 0.
+// O lane (c, h) register 4i+j holds query 8i+4h+j, feature 32 o + c.
+template <int NV, int D>
+__device__ __forceinline__ void store_rows(const FwdArgs& a, int bh, int qw0, int q_len, int n, int hh,
+                                           const v16f (&O)[NV], const float (&lq)[16], int cnt) {
+  const int Sq = a.Sq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int qq = qw0 + 8 * i + 4 * hh + j;
+      if (qq < Sq) {
+        const bool live = qq < q_len && lq[4 * i + j] > 0.0f;
+        const float inv = live ? 1.0f / lq[4 * i + j] : 0.0f;
+        uint16_t* orow = a.out + ((size_t)bh * Sq + qq) * D;
+#pragma unroll
+        for (int o = 0; o < NV; ++o) {
+          uint32_t uo = live ? __float_as_uint(O[o][4 * i + j] * inv) : 0u;
+          uo = (uo + 0x7FFFu + ((uo >> 16) & 1u)) >> 16;  // RNE to bf16 (finite values)
+          orow[32 * o + n] = (uint16_t)uo;
+        }
+      }
+    }
+  if (a.counts != nullptr && hh == 0 && qw0 + n < Sq) a.counts[(size_t)bh * Sq + qw0 + n] = qw0 + n < q_len ? cnt : 0;
 }
 
 // l accumulator: FP6 P -> 16x16 layout (v4f), FP8 P -> the layout of O (v16f)
@@ -376,10 +403,39 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   const int n = lane & 31, hh = lane >> 5;
   const int bh = blockIdx.y + blockIdx.z * a.H;
   const int Sq = a.Sq, Skv = a.Skv, nb32 = a.nb32;
-  const int qw0 = blockIdx.x * QWG + w * QW;
-  const int ns = (Skv + KS - 1) / KS;
-  const int nklast = Skv - (ns - 1) * KS;     // keys of the last step (1..64)
-  const int upart = nklast < KS ? ns - 1 : -1;  // the last step, when partial
+  // valid queries and keys of this batch (variable-length attention); with a
+  // causal mask query i sees keys k <= i + coff (queries aligned to the end
+  // of the keys)
+  const int q_len = a.q_lens ? min(max(a.q_lens[blockIdx.z], 0), Sq) : Sq;
+  const int kv_len = a.kv_lens ? min(max(a.kv_lens[blockIdx.z], 0), Skv) : Skv;
+  const int coff = kv_len - q_len;
+  // causal workgroups differ in length: the longest start first
+  const int q0 = (a.causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x) * QWG;
+  const int qw0 = q0 + w * QW;
+  // keys the workgroup reads: [0, kend), every key a valid query of it sees
+  int kend = q0 < q_len ? kv_len : 0;
+  if (a.causal) kend = max(min(kend, min(q0 + QWG, q_len) + coff), 0);
+  const int ns = (kend + KS - 1) / KS;
+  // keys [0, lim) are visible to this lane's query (lim <= 0: none).  Rows
+  // past q_len are computed unmasked and not stored.
+  const int lim = (a.causal && qw0 + n < q_len) ? min(kend, qw0 + n + coff + 1) : kend;
+  // steps from ums on hold a masked key for some row of the wave (its first
+  // row has the smallest limit): they take the exact path, which masks
+  const int lim_w = (a.causal && qw0 < q_len) ? min(kend, qw0 + coff + 1) : kend;
+  const int ums = max(lim_w, 0) / KS;
+  if (ns == 0) {
+    // no valid query or no visible key in the workgroup (uniform): zeros
+    v16f Oz[G::NV];
+    float lz[16];
+#pragma unroll
+    for (int o = 0; o < G::NV; ++o)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) Oz[o][k] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lz[k] = 0.0f;
+    store_rows<G::NV, D>(a, bh, qw0, q_len, n, hh, Oz, lz, 0);
+    return;
+  }
 
   // ---- DMA: this wave's loads (the same every step) and its two running
   // buffer descriptors (operand codes and scales of its side)
@@ -407,11 +463,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   const int lsc = __builtin_amdgcn_readfirstlane(dsl.lds), vsc_off = dsl.voff;
   uint64_t cbase = kside ? (uint64_t)(uintptr_t)(a.kc + (size_t)bh * Skv * G::QRB)
                          : (uint64_t)(uintptr_t)(a.vc + (size_t)bh * D * nb32 * G::VBB);
-  int crem = kside ? Skv * G::QRB : D * nb32 * G::VBB;
+  int crem = kside ? kend * G::QRB : D * nb32 * G::VBB;
   const int cstride = kside ? KS * G::QRB : 2 * G::VBB;
   uint64_t sbase = kside ? (uint64_t)(uintptr_t)(a.ks + (ks0 & ~(size_t)3))
                          : (uint64_t)(uintptr_t)(a.vs + (size_t)bh * nb32 * 128);
-  int srem = kside ? (((Skv + ko) * G::KSB + 3) & ~3) : nb32 * 128;
+  int srem = kside ? (((kend + ko) * G::KSB + 3) & ~3) : nb32 * 128;
   const int sstride = kside ? KS * G::KSB : 256;
   int snext = 0;  // next step to fetch
   const uint32_t lds0 = lds_addr(smem);
@@ -590,7 +646,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   auto ahead_max = [&](int s) -> float {
     v16f Sn[2];
     scores(Sn, s);
-    if (s == upart) mask(Sn, nklast);
+    if (s >= ums) mask(Sn, lim - s * KS);
     return max32(Sn);
   };
 
@@ -627,7 +683,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   bool any_fire = false;
   auto exact = [&](v16f (&S)[2], int u, float mnext, uint32_t (&dsc)[2], auto first_t) {
     constexpr bool FIRST = decltype(first_t)::value;
-    if (u == upart) mask(S, nklast);
+    if (u >= ums) mask(S, lim - u * KS);
     float m = max32(S);
     if constexpr (KV128) {
       if ((u & 1) == 0 && u + 1 < ns) m = __builtin_fmaxf(m, mnext);
@@ -636,7 +692,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     rho = 1.0f;
     any_fire = false;
     if (FIRST) {
-      set_C(T0 - m);
+      // a row that sees no key keeps P = 0 (its scores stay -inf)
+      set_C(m > -INFINITY ? T0 - m : 0.0f);
       shift(S, C);
     } else if (!KV128 || (u & 1) == 0) {
       const bool fire = m > Tg;
@@ -694,7 +751,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   {
     uint32_t dsc[2];
     exact(S, 0, mn, dsc, std::true_type{});
-    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, 0, hh, pA, dsc);
+    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, q_len, 0, hh, pA, dsc);
   }
   // V operands are read a phase ahead except with FP8 P (FP8 V operands
   // are 8 registers each; there the registers are not available)
@@ -716,7 +773,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     if constexpr (PRE_V) pv_of(pA, pS, vop);
     else pv_of(pA, pS, read_v(u - 1));
     const Check c = check(S, u, mn);
-    const bool rare = (u == upart) | (__ballot(!c.ok) != 0);
+    const bool rare = (u >= ums) | (__ballot(!c.ok) != 0);
     uint32_t wv[16], dsc[2];
     pack_b(S, wv);
     v8i pAf;
@@ -740,7 +797,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       exact(S, u, mn, dsc, std::false_type{});
       if (any_fire) rescale<PE, NV>(O, L, rho, lane);
     }
-    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, u * KS, hh, pA, dsc);
+    if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, q_len, u * KS, hh, pA, dsc);
     if constexpr (PRE_V) vop = read_v(u);
     if constexpr (KV128) {
       if (((u + 1) & 1) == 0 && u + 2 < ns) mn = ahead_max(u + 2);
@@ -765,23 +822,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       for (int j = 0; j < 4; ++j) lq[4 * i + j] = wshfl(L[j], srcl);
     }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int qq = qw0 + 8 * i + 4 * hh + j;
-      if (qq < Sq) {
-        const float inv = 1.0f / lq[4 * i + j];
-        uint16_t* orow = a.out + ((size_t)bh * Sq + qq) * D;
-#pragma unroll
-        for (int o = 0; o < NV; ++o) {
-          uint32_t uo = __float_as_uint(O[o][4 * i + j] * inv);
-          uo = (uo + 0x7FFFu + ((uo >> 16) & 1u)) >> 16;  // RNE to bf16 (finite values)
-          orow[32 * o + n] = (uint16_t)uo;
-        }
-      }
-    }
-  if (a.counts != nullptr && hh == 0 && qw0 + n < Sq) a.counts[(size_t)bh * Sq + qw0 + n] = cnt;
+  store_rows<NV, D>(a, bh, qw0, q_len, n, hh, O, lq, cnt);
 }
 
 template <int QK, int VE, int PE, int D>

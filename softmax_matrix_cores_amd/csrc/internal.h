@@ -23,6 +23,9 @@ struct FwdArgs {
   float T0, Tg;  // fl32(128*127 - c), fl32(128*(127+tau) - c)
   int kv128;     // gate tile = 128 keys (else 64)
   int fitmax;
+  int causal;              // query i sees keys k <= i + kv_len - q_len
+  const int32_t* q_lens;   // [B] valid queries per batch, or null (Sq)
+  const int32_t* kv_lens;  // [B] valid keys per batch, or null (Skv)
 };
 
 hipError_t launch_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld, int axis,

@@ -84,11 +84,14 @@ def p_mismatch(gc, gs, oc, os_) -> float:
 
 
 def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=None, kv_tile=None,
-             check_quant=True):
+             check_quant=True, causal=False, q_lens=None, kv_lens=None):
     """Full comparison on workload w.  rows: oracle row sample (None = all rows).
+    causal / q_lens / kv_lens: masks ([B] lists), sent to both sides.
     Returns a dict of metrics; asserts nothing."""
+    masked = causal or q_lens is not None or kv_lens is not None
     log(f"[case] {w.name} B={w.B} H={w.H} Sq={w.Sq} Skv={w.Skv} D={w.D} {w.qk_elem}/{w.v_elem}/{w.p_elem} "
-        f"tau={w.tau if tau is None else tau} kv_tile={w.kv_tile if kv_tile is None else kv_tile}")
+        f"tau={w.tau if tau is None else tau} kv_tile={w.kv_tile if kv_tile is None else kv_tile}"
+        + (f" causal={causal} q_lens={q_lens} kv_lens={kv_lens}" if masked else ""))
     q, k, v = (x.cpu() for x in W.make_inputs(w, device="cuda:0"))
     tau_ = w.tau if tau is None else tau
     kvt = w.kv_tile if kv_tile is None else kv_tile
@@ -103,8 +106,14 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
         pc = torch.zeros(r1 - r0, s32, dtype=torch.uint8, device="cuda:0")
         ps = torch.zeros(r1 - r0, s32 // 32, dtype=torch.uint8, device="cuda:0")
         pd = (dump_head[0], dump_head[1], r0, r1, pc, ps)
+    mk = {}
+    if masked:
+        dev = torch.device("cuda:0")
+        mk = dict(causal=causal,
+                  q_lens=None if q_lens is None else torch.tensor(q_lens, dtype=torch.int32, device=dev),
+                  kv_lens=None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device=dev))
     out = fs.forward(Qg, Kg, Vg, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=tau_, kv_tile=kvt,
-                     counts=counts, p_dump=pd)
+                     counts=counts, p_dump=pd, **mk)
     torch.cuda.synchronize()
     log(f"[case] {w.name}: GPU done")
     # oracle
@@ -115,7 +124,8 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
         res["quant_v"] = same_bytes(Vg, Vo, axis=1)
     p = oracle_params(O, w, tau=tau_, kv_tile=kvt)
     row_ids = None if rows is None else np.asarray(rows, dtype=np.int64)
-    r = O.forward(p, Qo, Ko, Vo, rows=row_ids)
+    omk = dict(causal=causal, q_lens=q_lens, kv_lens=kv_lens) if masked else {}
+    r = O.forward(p, Qo, Ko, Vo, rows=row_ids, **omk)
     gout = out.float().cpu().numpy().reshape(-1, w.D)
     gcnt = counts.cpu().numpy().ravel()
     if row_ids is not None:
@@ -125,10 +135,15 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
     res["count_mismatch_rows"] = int((gcnt != r["counts"]).sum())
     res["total_counts"] = int(r["counts"].sum())
     res["finite"] = bool(np.isfinite(gout).all())
+    if masked:
+        # rows the oracle leaves empty (no visible key, or past q_len) must be exactly 0
+        dead = r["l"] == 0
+        res["dead_rows"] = int(dead.sum())
+        res["dead_rows_nonzero"] = int((gout[dead] != 0).any(axis=1).sum()) + int((gcnt[dead] != 0).sum())
     if dump_rows is not None:
         b, h, r0, r1 = pd[:4]
         drows = (b * w.H + h) * w.Sq + np.arange(r0, r1)
-        rd = O.forward(p, Qo, Ko, Vo, rows=drows, want_p=True)
+        rd = O.forward(p, Qo, Ko, Vo, rows=drows, want_p=True, **omk)
         res["p_mismatch"] = p_mismatch(pd[4].cpu().numpy(), pd[5].cpu().numpy(), rd["p_codes"], rd["p_scales"])
     log(f"[case] {w.name}: {res}")
     return res
@@ -143,6 +158,7 @@ def assert_ok(res: dict, defer_p: bool = False):
     assert res["finite"], res
     assert res["rel_frob"] <= REL_FROB_TOL, res
     assert res["count_mismatch_rows"] == 0, res
+    assert res.get("dead_rows_nonzero", 0) == 0, res
     if not defer_p:
         check_p(res)
 

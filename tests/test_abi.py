@@ -99,3 +99,23 @@ def test_bf16_baseline_validation():
     assert B(16, 16, 16, 1, 1, 8, 0, 128, ctypes.c_float(0.1), 16, None) == -1
     assert B(8, 16, 16, 1, 1, 8, 8, 128, ctypes.c_float(0.1), 16, None) == -3
     assert B(16, 16, 16, 1, 1, 0, 8, 128, ctypes.c_float(0.1), 16, None) == 0
+
+
+def test_masked_forward_validation_rejects_before_launch():
+    k1 = _mx(prescale=1.0)
+    v1 = _mx(prescale=1.0)
+    M = fs.lib().fsattn_forward_masked
+
+    def call(mask, p=None):
+        p = _params() if p is None else p
+        q = _mx()
+        return M(ctypes.byref(p), ctypes.byref(mask) if mask is not None else None, ctypes.byref(q),
+                 ctypes.byref(k1), ctypes.byref(v1), 16, None)
+
+    assert M(None, None, None, None, None, None, None) == -1
+    assert call(fs._Mask(2, None, None)) == -1                        # causal must be 0 or 1
+    assert call(fs._Mask(1, 2, None)) == -3                           # q_lens alignment
+    assert call(fs._Mask(0, None, 6)) == -3                           # kv_lens alignment
+    assert call(fs._Mask(1, 16, 16), _params(D=96)) == -1             # the fsattn_forward checks still apply
+    assert call(fs._Mask(1, 16, 16), _params(Sq=0)) == 0              # empty: OK, no launch
+    assert call(None, _params(B=0)) == 0                              # NULL mask = fsattn_forward
