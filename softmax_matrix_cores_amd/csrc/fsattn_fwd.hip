@@ -221,6 +221,13 @@ __device__ Dma dma_scale(bool kside, int wj, int lane, int ko) {
   return Dma{G::VS_OFF + 4 * lane, 4 * lane};
 }
 
+// P operand registers: FP6 P uses 6 (kept as such across the loop and
+// widened at each product, so that no copy carries unused registers)
+template <int PE> struct POp { typedef v6i T; };
+template <> struct POp<E4M3> { typedef v8i T; };
+__device__ __forceinline__ v8i widen(const v6i& p) { return v8i{p[0], p[1], p[2], p[3], p[4], p[5], 0, 0}; }
+__device__ __forceinline__ const v8i& widen(const v8i& p) { return p; }
+
 // E8M0 of a P block from its largest BF16 pattern (integer exponent math)
 template <int PELEM>
 __device__ __forceinline__ uint32_t p_scale(uint32_t bmax) {
@@ -261,7 +268,8 @@ __device__ __forceinline__ float max32(const v16f (&S)[2]) { return __builtin_fm
 // FP6 P: the lane's 32 keys are one block.  FP8 P: elements 0-15 belong to
 // block 0 of the step, 16-31 to block 1, each block spanning lanes q and q+32.
 template <int PE, bool FAST>
-__device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, float m1, int lane, v8i& pA, int& pS,
+__device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, float m1, int lane,
+                                         typename POp<PE>::T& pA, int& pS,
                                          uint32_t (&dsc)[2]) {
   if constexpr (!Opd<PE>::split) {
     const float tm = __builtin_fmaxf(m0, m1);
@@ -282,7 +290,7 @@ __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, floa
     const float X = FAST ? __uint_as_float(sc << 23) : e8m0_to_float(sc);
     if constexpr (PE == E2M3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(x, X);
     else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(x, X);
-    pA = v8i{r[0], r[1], r[2], r[3], r[4], r[5], 0, 0};
+    pA = r;
     pS = (int)sc;
     dsc[0] = sc;
     dsc[1] = sc;
@@ -309,7 +317,8 @@ __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, floa
 
 // optional P dump (debug): one code byte per key and the E8M0 per 32 keys
 template <int PE>
-__device__ __forceinline__ void dump_p(const FwdArgs& a, int bh, int qq, int q_len, int k0, int hh, const v8i& pA,
+__device__ __forceinline__ void dump_p(const FwdArgs& a, int bh, int qq, int q_len, int k0, int hh,
+                                       const typename POp<PE>::T& pA,
                                        const uint32_t (&dsc)[2]) {
   if (bh != a.pd_bh || qq < a.pd_row0 || qq >= a.pd_row1 || qq >= q_len) return;
   const int nb32 = a.nb32;
@@ -395,6 +404,7 @@ template <int QK, int VE, int PE, int D, bool KV128, bool DUMP>
 __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   using G = Geo<QK, VE, D>;
   using LT = typename LAcc<PE>::T;
+  using PT = typename POp<PE>::T;
   constexpr int NV = G::NV;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
 
@@ -616,7 +626,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     return v;
   };
   // O += P V (feature block o) and l += P 1
-  auto pv_of = [&](const v8i& pa, int ps, const VOps& v) {
+  auto pv_of = [&](const PT& pa6, int ps, const VOps& v) {
+    const v8i pa = widen(pa6);
     O[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, v.op[0], O[0], PE, VE, 0, ps, 0, v.vsc);
     O[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, v.op[1], O[1], PE, VE, 0, ps, 1, v.vsc);
     if constexpr (NV > 2) {
@@ -650,7 +661,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     return max32(Sn);
   };
 
-  v8i pA = {0, 0, 0, 0, 0, 0, 0, 0};
+  PT pA = {};
   int pS = 127;
 
   // fast-path test of step u: the lane's maxima over its two key groups, and
@@ -704,7 +715,12 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
         rho = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
       }
       any_fire = __ballot(fire) != 0;
-      if (any_fire) set_C(C - delta);
+      if (any_fire) {
+        // in place: Cv holds C in every register
+        C = C - delta;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) Cv[k] = Cv[k] - delta;
+      }
     }
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
@@ -776,7 +792,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     const bool rare = (u >= ums) | (__ballot(!c.ok) != 0);
     uint32_t wv[16], dsc[2];
     pack_b(S, wv);
-    v8i pAf;
+    PT pAf;
     int pSf;
     p_from_w<PE, true>(wv, c.m0, c.m1, lane, pAf, pSf, dsc);
     // computed here on every step (not sunk into the fast branch)
