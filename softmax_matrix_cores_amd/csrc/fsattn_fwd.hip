@@ -738,6 +738,39 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     p_from_w<PE, false>(wv, mx0, mx1, lane, pA, pS, dsc);
   };
 
+  // gate-only rare step (64-key gate tiles, one P block per lane, no masked
+  // key): the fast-path test failed only because a row's maximum passed the
+  // gate.  The row maximum, the shift and the shifted lane maxima follow from
+  // the test's lane maxima; when every lane's shifted maximum still clears the
+  // flush bound the fast conversion is exact on the shifted scores, and the
+  // exact path is skipped.  Returns false (nothing changed) otherwise.
+  auto gate_fast = [&](v16f (&S)[2], const Check& c, uint32_t (&dsc)[2]) -> bool {
+    const float tm = __builtin_fmaxf(c.m0, c.m1);
+    const float mrow = __builtin_fmaxf(tm, wshfl(tm, lane ^ 32));
+    const bool fire = mrow > Tg;
+    const float delta = fire ? mrow - T0 : 0.0f;
+    // max(fl32(s - delta)) = fl32(max s - delta): the maps are monotonic
+    const float m0 = c.m0 - delta, m1 = c.m1 - delta;
+    const bool ok = fire ? __builtin_fmaxf(m0, m1) >= PFlush<PE>::t : c.ok;
+    if (__ballot(!ok) != 0) return false;
+    rho = 1.0f;
+    if (fire) {
+      shift(S, -delta);
+      cnt += 1;
+      rho = __builtin_amdgcn_exp2f(-delta * (1.0f / 128.0f));
+    }
+    any_fire = __ballot(fire) != 0;
+    if (any_fire) {
+      C = C - delta;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) Cv[k] = Cv[k] - delta;
+    }
+    uint32_t wv[16];
+    pack_b(S, wv);
+    p_from_w<PE, true>(wv, m0, m1, lane, pA, pS, dsc);
+    return true;
+  };
+
   // one barrier per step: before it each wave waits for its loads of the
   // steps up to u + 1 (u + 2 with 128-key gate tiles, whose odd step is read
   // one step early); after it the loads of step u + PF go into the slot of
@@ -810,7 +843,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     pA = pAf;
     pS = pSf;
     if (rare) {
-      exact(S, u, mn, dsc, std::false_type{});
+      bool done = false;
+      if constexpr (!KV128 && !Opd<PE>::split) done = u < ums && gate_fast(S, c, dsc);
+      if (!done) exact(S, u, mn, dsc, std::false_type{});
       if (any_fire) rescale<PE, NV>(O, L, rho, lane);
     }
     if constexpr (DUMP) dump_p<PE>(a, bh, qw0 + n, q_len, u * KS, hh, pA, dsc);
