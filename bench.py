@@ -15,6 +15,10 @@ Inputs are resident in HBM before timing starts.  Reported:
                workload, in the same unit
   causal       (video workloads) the fused kernel under a causal mask on the
                same inputs: 4*B*H*D*S(S+1)/2 flops (visible pairs only)
+  schedule     (video workloads) the per-call precision schedule of the pages
+               (MXFP6 for the first and last 3 of 20 denoising steps, MXFP4 for
+               the 14 between): the time-weighted mean of the two formats'
+               whole-path steps and kernels
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video-mxfp6]
 """
@@ -265,6 +269,17 @@ def main():
                                        "mx_mfma_util": round(c_tf / _peak_for(w), 4), "rollbacks": c_cnt,
                                        "flops": c_flops,
                                        "time_vs_unmasked": round(c_ms / main_res[1], 4)}
+
+    if "video-mxfp6" in formats and "video-mxfp4" in formats:
+        f6, f4 = formats["video-mxfp6"], formats["video-mxfp4"]
+        sched = {"steps_mxfp6": 6, "steps_mxfp4": 14}
+        for key in ("step_ms", "kernel_ms"):
+            sched[key] = round((6 * f6[key] + 14 * f4[key]) / 20, 4)
+        sched["kernel_tflops"] = round(w.flops / (sched["kernel_ms"] * 1e-3) / 1e12, 2)
+        if bf16_ms is not None:
+            sched["speedup_vs_bf16_kernel"] = round(bf16_ms / sched["kernel_ms"], 3)
+            sched["speedup_vs_bf16_incl_quant"] = round(bf16_ms / sched["step_ms"], 3)
+        formats["video-schedule-6xmxfp6-14xmxfp4"] = sched
 
     st_ms, fwd_ms, rec = main_res
     value = w.flops / (st_ms * 1e-3) / 1e12
