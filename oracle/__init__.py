@@ -74,6 +74,8 @@ def lib():
         L.fso_block_bytes.argtypes = [ctypes.c_int]
         L.fso_quantize_mx.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, P, P]
+        L.fso_quantize_mx_rmsnorm.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                              P, ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, P, P]
         L.fso_stage1.restype = ctypes.c_uint16
         L.fso_stage1.argtypes = [ctypes.c_float]
         L.fso_forward.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P, ctypes.c_int64, P, P, P, P, P]
@@ -146,6 +148,26 @@ def quantize_mx(x_bf16: np.ndarray, block_axis: int, elem: int, prescale: float 
                                _ptr(codes), _ptr(scales))
     if rc != 0:
         raise ValueError(f"fso_quantize_mx failed ({rc})")
+    return codes, scales
+
+
+def quantize_mx_rmsnorm(x_bf16: np.ndarray, elem: int, prescale: float = 1.0, weight=None, eps: float = 1e-6,
+                        rule: int = SCALE_FITMAX) -> tuple[np.ndarray, np.ndarray]:
+    """RMS-normalised rows, then the prescale and MX quantization (block_axis 0).
+    x_bf16: uint16 [n_mat, rows, cols]; weight: float32 [cols] or None."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    assert x.ndim == 3
+    n_mat, rows, cols = x.shape
+    bb = block_bytes(elem)
+    codes = np.zeros((n_mat, rows, cols // 32 * bb), np.uint8)
+    scales = np.zeros((n_mat, rows, cols // 32), np.uint8)
+    w = None if weight is None else np.ascontiguousarray(weight, dtype=np.float32)
+    if w is not None and w.shape != (cols,):
+        raise ValueError("weight must have cols entries")
+    rc = lib().fso_quantize_mx_rmsnorm(_ptr(x), n_mat, rows, cols, cols, _ptr(w), ctypes.c_float(eps),
+                                       ctypes.c_float(prescale), elem, rule, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"fso_quantize_mx_rmsnorm failed ({rc})")
     return codes, scales
 
 

@@ -239,10 +239,33 @@ typedef struct {
   int block_axis, elem, rule;
   float prescale;
   uint8_t *codes, *scales;
+  int rmsnorm;          /* axis 0 only: RMS-normalise each row first (R23) */
+  const float* weight;  /* [cols] per-feature weight, or NULL */
+  float eps;
   int64_t nunits; /* axis 0: n_mat*rows rows; axis 1: n_mat*cols columns */
   int64_t next;
   pthread_mutex_t mu;
 } quant_job_t;
+
+/* RMS factor of one row (R23): the squares summed in binary64 block by block
+ * (each block's 32 squares in index order, then the block sums in order);
+ * r = fl32(1 / sqrt(ss / cols + eps)) with the quotient, the root and the
+ * reciprocal in binary64; r = 0 when ss / cols + eps is 0 (a zero row stays
+ * zero).  The squares of bf16 values are exact in binary64. */
+static float rms_factor(const uint16_t* s, int64_t cols, float eps) {
+  double ss = 0.0;
+  for (int64_t g = 0; g < cols / 32; ++g) {
+    double b = 0.0;
+    for (int j = 0; j < 32; ++j) {
+      double v = bf16_to_double(s[g * 32 + j]);
+      b += v * v;
+    }
+    ss += b;
+  }
+  double a = ss / (double)cols + (double)eps;
+  if (a == 0.0) return 0.0f;
+  return (float)(1.0 / sqrt(a));
+}
 
 /* quantize every block of one unit (a row on axis 0, a column on axis 1) */
 static void quant_unit(const quant_job_t* J, int64_t u) {
@@ -252,9 +275,16 @@ static void quant_unit(const quant_job_t* J, int64_t u) {
   if (J->block_axis == 0) {
     int64_t m = u / J->rows, r = u % J->rows, nb = J->cols / 32;
     const uint16_t* s = J->src + m * J->rows * J->ld + r * J->ld;
+    const float rf = J->rmsnorm ? rms_factor(s, J->cols, J->eps) : 1.0f;
     for (int64_t g = 0; g < nb; ++g) {
       for (int j = 0; j < 32; ++j) {
         double v = bf16_to_double(s[g * 32 + j]);
+        if (J->rmsnorm) {
+          /* y = fl32(fl32(x r) w), then the prescale like any operand */
+          float y = (float)v * rf;
+          if (J->weight) y = y * J->weight[g * 32 + j];
+          v = (double)y;
+        }
         x[j] = (J->prescale == 1.0f) ? v : (double)(float)((double)J->prescale * v);
       }
       fso_mxq_block(J->elem, J->rule, x, 32, c, J->scales + u * nb + g);
@@ -290,14 +320,16 @@ static void* quant_worker(void* arg) {
   return NULL;
 }
 
-int fso_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
-                    int block_axis, float prescale, int elem, int rule,
-                    uint8_t* codes, uint8_t* scales) {
+static int quantize_impl(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
+                         int block_axis, float prescale, int elem, int rule, uint8_t* codes, uint8_t* scales,
+                         int rmsnorm, const float* weight, float eps) {
   if (!valid_elem(elem) || (block_axis != 0 && block_axis != 1) || n_mat < 0 || rows < 0 || cols < 0 ||
       ld < cols)
     return FSO_EINVAL;
   if (block_axis == 0 && cols % 32) return FSO_EINVAL;
+  if (rmsnorm && (block_axis != 0 || !(eps >= 0.0f))) return FSO_EINVAL;
   quant_job_t J;
+  J.rmsnorm = rmsnorm; J.weight = weight; J.eps = eps;
   J.src = src; J.n_mat = n_mat; J.rows = rows; J.cols = cols; J.ld = ld;
   J.block_axis = block_axis; J.elem = elem; J.rule = rule; J.prescale = prescale;
   J.codes = codes; J.scales = scales;
@@ -312,6 +344,18 @@ int fso_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t co
   for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
   pthread_mutex_destroy(&J.mu);
   return FSO_OK;
+}
+
+int fso_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
+                    int block_axis, float prescale, int elem, int rule,
+                    uint8_t* codes, uint8_t* scales) {
+  return quantize_impl(src, n_mat, rows, cols, ld, block_axis, prescale, elem, rule, codes, scales, 0, NULL, 0.0f);
+}
+
+int fso_quantize_mx_rmsnorm(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
+                            const float* weight, float eps, float prescale, int elem, int rule,
+                            uint8_t* codes, uint8_t* scales) {
+  return quantize_impl(src, n_mat, rows, cols, ld, 0, prescale, elem, rule, codes, scales, 1, weight, eps);
 }
 
 /* ------------------------------------------------------------------------ */

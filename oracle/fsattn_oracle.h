@@ -96,6 +96,22 @@ int fso_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t co
                     int block_axis, float prescale, int elem, int rule,
                     uint8_t* codes, uint8_t* scales);
 
+/*
+ * Fused producer step before the path (RMS-normalised Q/K rows, then the
+ * prescale and MX quantization), reading R23: for each row x of `cols`
+ * bf16 values (block_axis 0 layout):
+ *   ss = sum of x_j^2 in binary64, each 32-block's squares in index order,
+ *        then the block sums in order;
+ *   r  = fl32(1 / sqrt(ss / cols + eps)), quotient/root/reciprocal in
+ *        binary64; r = 0 when ss / cols + eps is 0;
+ *   y_j = fl32(fl32(x_j r) w_j) (w = NULL: no weight);
+ *   then y is quantized like fso_quantize_mx input: fl32(prescale y), MX.
+ * eps >= 0.
+ */
+int fso_quantize_mx_rmsnorm(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
+                            const float* weight, float eps, float prescale, int elem, int rule,
+                            uint8_t* codes, uint8_t* scales);
+
 /* Schraudolph stage 1: fp32 folded score -> BF16 bit pattern */
 uint16_t fso_stage1(float t);
 
