@@ -15,6 +15,9 @@ Inputs are resident in HBM before timing starts.  Reported:
                workload, in the same unit
   causal       (video workloads) the fused kernel under a causal mask on the
                same inputs: 4*B*H*D*S(S+1)/2 flops (visible pairs only)
+  prologue     (video workloads) the producer step fused into the quantizer:
+               RMS-normalised Q and K rows (per-feature weight) quantized in
+               one pass, against a torch RMS norm followed by the quantizer
   schedule     (video workloads) the per-call precision schedule of the pages
                (MXFP6 for the first and last 3 of 20 denoising steps, MXFP4 for
                the 14 between): the time-weighted mean of the two formats'
@@ -135,6 +138,45 @@ def time_fused_causal(fs, w, q, k, v, steps, warmup):
     return sum(ts) / len(ts), int(counts.sum().item())
 
 
+def time_prologue(fs, w, q, k, steps):
+    """Fused RMS-norm + quantization of Q and K against torch's norm + the quantizer (ms per Q+K pair)."""
+    import torch
+
+    st = torch.cuda.current_stream()
+    g = torch.Generator(device=q.device).manual_seed(7)
+    wq = torch.empty(w.D, device=q.device).uniform_(0.5, 2.0, generator=g)
+    wk = torch.empty(w.D, device=q.device).uniform_(0.5, 2.0, generator=g)
+    pre = fs.fold_prescale(w.sigma)
+
+    def fused():
+        fs.quantize_mx_rmsnorm(q, w.qk_elem, prescale=pre, weight=wq)
+        fs.quantize_mx_rmsnorm(k, w.qk_elem, weight=wk)
+
+    def unfused():
+        for x, wt, ps in ((q, wq, pre), (k, wk, 1.0)):
+            xf = x.float()
+            xn = (xf * torch.rsqrt(xf.square().mean(-1, keepdim=True) + 1e-6) * wt).to(torch.bfloat16)
+            fs.quantize_mx(xn, 0, w.qk_elem, prescale=ps)
+
+    res = {}
+    for name, fn in (("fused_ms", fused), ("unfused_ms", unfused)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(steps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        res[name] = round(a.elapsed_time(b) / steps, 4)
+    n = 2 * q.numel()
+    bits = {"e4m3": 8, "e2m3": 6, "e2m1": 4}[w.qk_elem]
+    hbm = n * 2 + n * bits / 8 + n / 32  # bf16 in, codes and scales out
+    res["fused_hbm_GBps"] = round(hbm / (res["fused_ms"] * 1e-3) / 1e9, 1)
+    res["speedup"] = round(res["unfused_ms"] / res["fused_ms"], 2)
+    return res
+
+
 def time_bf16(fs, w, q, k, v, steps, warmup):
     import torch
 
@@ -200,6 +242,7 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-causal", action="store_true", help="skip the causal-mask leg")
+    ap.add_argument("--no-prologue", action="store_true", help="skip the fused-prologue timing")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration for profiles)")
@@ -270,6 +313,12 @@ def main():
                                        "flops": c_flops,
                                        "time_vs_unmasked": round(c_ms / main_res[1], 4)}
 
+    if not args.no_prologue and w.name.startswith("video-"):
+        print("[bench] fused prologue", file=sys.stderr, flush=True)
+        line_prologue = time_prologue(fs, w, q, k, max(3, args.steps // 2))
+    else:
+        line_prologue = None
+
     if "video-mxfp6" in formats and "video-mxfp4" in formats:
         f6, f4 = formats["video-mxfp6"], formats["video-mxfp4"]
         sched = {"steps_mxfp6": 6, "steps_mxfp4": 14}
@@ -297,6 +346,8 @@ def main():
                      "kernel": "fsattn_fwd_kernel", "flops_per_launch": w.flops},
         "formats": formats,
     }
+    if line_prologue is not None:
+        line["prologue"] = line_prologue
     if bf16_ms is not None:
         line["bf16_baseline"] = {"kernel_ms": round(bf16_ms, 4),
                                  "tflops": round(w.flops / (bf16_ms * 1e-3) / 1e12, 2),

@@ -112,6 +112,34 @@ int64_t fsattn_mx_scales_bytes(int64_t n_mat, int64_t rows, int64_t cols, int bl
 int fsattn_quantize_mx(const void* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld, int block_axis,
                        float prescale, int elem, int rule, void* codes_out, uint8_t* scales_out, void* stream);
 
+/*
+ * fsattn_quantize_mx_rmsnorm -- the producer step before the path for
+ * qk-normed models, fused into one pass: RMS-normalise each row of Q or K,
+ * apply a per-feature weight, then the prescale and MX quantization along the
+ * row (block_axis 0 output layout, as fsattn_quantize_mx).  The pages' model
+ * (a video diffusion transformer, "Fused-Softmax shifts an AI attention
+ * bottleneck onto faster GPU hardware", paragraph 9) normalises Q and K before
+ * attention; fusing it removes a full read and write of Q and K.
+ *
+ * Per row x of `cols` bf16 values:
+ *   ss = sum of x_j^2 in binary64 (each 32-block's squares in index order,
+ *        then the block sums in order);
+ *   r  = fl32(1 / sqrt(ss / cols + eps)), quotient, root and reciprocal in
+ *        binary64, correctly rounded; r = 0 when ss / cols + eps is 0;
+ *   y_j = fl32(fl32(x_j r) w_j), then fl32(prescale y_j) is MX-quantized like
+ *        a fsattn_quantize_mx input (the same rule and rounding).
+ *  src      device bf16 [n_mat][rows][cols], row stride ld elements.
+ *  weight   optional DEVICE float [cols] (NULL: no weight).
+ *  eps      >= 0, finite.
+ *  Errors: FSATTN_E_INVALID_ARG (null, negative sizes, ld < cols, cols % 32,
+ *  bad enum, eps < 0, non-finite eps or prescale), FSATTN_E_UNSUPPORTED
+ *  (cols not a power of two in [32, 2048]), FSATTN_E_ALIGNMENT (src not
+ *  2-byte, codes_out not 16-byte, weight not 4-byte aligned), FSATTN_E_HIP.
+ */
+int fsattn_quantize_mx_rmsnorm(const void* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
+                               const float* weight, float eps, float prescale, int elem, int rule, void* codes_out,
+                               uint8_t* scales_out, void* stream);
+
 /* An MX operand as produced by fsattn_quantize_mx. */
 typedef struct {
   int elem;              /* fsattn_elem */

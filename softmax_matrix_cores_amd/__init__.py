@@ -26,7 +26,8 @@ SCALE_FITMAX, SCALE_OCP_FLOOR = 0, 1
 # every symbol include/fsattn.h declares
 ABI_SYMBOLS = (
     "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
-    "fsattn_quantize_mx", "fsattn_forward", "fsattn_forward_masked", "fsattn_forward_bf16_baseline",
+    "fsattn_quantize_mx", "fsattn_quantize_mx_rmsnorm", "fsattn_forward", "fsattn_forward_masked",
+    "fsattn_forward_bf16_baseline",
 )
 
 
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.fsattn_mx_scales_bytes.argtypes = [I64, I64, I64, I]
         L.fsattn_quantize_mx.restype = I
         L.fsattn_quantize_mx.argtypes = [V, I64, I64, I64, I64, I, ctypes.c_float, I, I, V, V, V]
+        L.fsattn_quantize_mx_rmsnorm.restype = I
+        L.fsattn_quantize_mx_rmsnorm.argtypes = [V, I64, I64, I64, I64, V, ctypes.c_float, ctypes.c_float, I, I, V,
+                                                 V, V]
         L.fsattn_forward.restype = I
         L.fsattn_forward.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
                                      ctypes.POINTER(_MxTensor), V, V]
@@ -147,6 +151,34 @@ def quantize_mx(x: torch.Tensor, block_axis: int, elem, prescale: float = 1.0, r
     st = lib().fsattn_quantize_mx(x.data_ptr(), n_mat, rows, cols, cols, block_axis, ctypes.c_float(prescale), e,
                                   rule, codes.data_ptr(), scales.data_ptr(), _stream(stream))
     _check("fsattn_quantize_mx", st)
+    return MXTensor(codes, scales, e, float(torch.tensor(prescale, dtype=torch.float32)))
+
+
+def quantize_mx_rmsnorm(x: torch.Tensor, elem, prescale: float = 1.0, weight: torch.Tensor | None = None,
+                        eps: float = 1e-6, rule: int = SCALE_FITMAX, stream=None,
+                        out: MXTensor | None = None) -> MXTensor:
+    """RMS-normalise the rows of a contiguous bf16 CUDA tensor [..., rows, cols] (optional float32
+    weight [cols]), then apply the prescale and MX-quantize along the rows (block_axis 0)."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda:
+        raise TypeError("quantize_mx_rmsnorm expects a bf16 CUDA tensor")
+    x = x.contiguous()
+    rows, cols = x.shape[-2], x.shape[-1]
+    n_mat = x.numel() // max(1, rows * cols) if rows * cols else 0
+    e = _elem(elem)
+    if weight is not None and (weight.dtype != torch.float32 or weight.device != x.device or
+                               weight.shape != (cols,) or not weight.is_contiguous()):
+        raise ValueError("weight must be a contiguous float32 [cols] tensor on the input's device")
+    cb, sb = mx_sizes(e, n_mat, rows, cols, 0)
+    if out is None:
+        codes = torch.empty(cb, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(sb, dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out.codes, out.scales
+    st = lib().fsattn_quantize_mx_rmsnorm(x.data_ptr(), n_mat, rows, cols, cols,
+                                          weight.data_ptr() if weight is not None else None, ctypes.c_float(eps),
+                                          ctypes.c_float(prescale), e, rule, codes.data_ptr(), scales.data_ptr(),
+                                          _stream(stream))
+    _check("fsattn_quantize_mx_rmsnorm", st)
     return MXTensor(codes, scales, e, float(torch.tensor(prescale, dtype=torch.float32)))
 
 

@@ -95,6 +95,26 @@ int fsattn_quantize_mx(const void* src, int64_t n_mat, int64_t rows, int64_t col
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
 }
 
+int fsattn_quantize_mx_rmsnorm(const void* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
+                               const float* weight, float eps, float prescale, int elem, int rule, void* codes_out,
+                               uint8_t* scales_out, void* stream) {
+  if (!elem_bits(elem) || (rule != FSATTN_SCALE_FITMAX && rule != FSATTN_SCALE_OCP_FLOOR)) return FSATTN_E_INVALID_ARG;
+  if (n_mat < 0 || rows < 0 || cols < 0 || ld < cols) return FSATTN_E_INVALID_ARG;
+  if (cols % 32) return FSATTN_E_INVALID_ARG;
+  if (!isfinite(prescale) || !(eps >= 0.0f) || !isfinite(eps)) return FSATTN_E_INVALID_ARG;
+  // a row's blocks are the consecutive lanes of one wave
+  if (cols > 2048 || (cols & (cols - 1)) != 0) return FSATTN_E_UNSUPPORTED;
+  if (n_mat == 0 || rows == 0 || cols == 0) return FSATTN_OK;
+  if (!src || !codes_out || !scales_out) return FSATTN_E_INVALID_ARG;
+  if (!aligned(src, 2) || !aligned(codes_out, 16) || !aligned(weight, 4)) return FSATTN_E_ALIGNMENT;
+  if (nblocks(n_mat, rows, cols, 0) > ((int64_t)1 << 40)) return FSATTN_E_UNSUPPORTED;
+  hipError_t e = fsattn::launch_quantize_mx_rmsnorm(static_cast<const uint16_t*>(src), n_mat * rows, cols, ld, weight,
+                                                    eps, prescale, elem, rule == FSATTN_SCALE_FITMAX,
+                                                    static_cast<uint8_t*>(codes_out), scales_out,
+                                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
+}
+
 int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
                           const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream) {
   if (!p || !q || !k || !v) return FSATTN_E_INVALID_ARG;

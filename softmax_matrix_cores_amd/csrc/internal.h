@@ -31,6 +31,9 @@ struct FwdArgs {
 hipError_t launch_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld, int axis,
                               float prescale, int elem, bool fitmax, uint8_t* codes, uint8_t* scales,
                               hipStream_t stream);
+hipError_t launch_quantize_mx_rmsnorm(const uint16_t* src, int64_t nrows, int64_t cols, int64_t ld,
+                                      const float* weight, float eps, float prescale, int elem, bool fitmax,
+                                      uint8_t* codes, uint8_t* scales, hipStream_t stream);
 bool fwd_supported(int qk, int ve, int pe);
 hipError_t launch_fsattn_fwd(const FwdArgs& a, int B, int D, int qk, int ve, int pe, hipStream_t s);
 hipError_t launch_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int B, int H,

@@ -172,6 +172,84 @@ __global__ void __launch_bounds__(256) mxq_axis0_kernel(const uint16_t* __restri
   scales[blk] = (uint8_t)code;
 }
 
+// Fused producer step for qk-normed models: RMS-normalise each row (weight w
+// per feature), then the prescale and MX quantization along the row.  One
+// lane per 32-element block as above; the nb = cols / 32 lanes of a row are
+// consecutive lanes of one wave (nb a power of two, at most 64).  Per row:
+//   ss = the squares summed in binary64 (each block's in index order, then the
+//        block sums in order: every lane adds them in the same order, so the
+//        row's lanes agree bit for bit), exact squares of bf16 values;
+//   r  = fl32(1 / sqrt(ss / cols + eps)) in binary64 (correctly rounded root
+//        and quotient), r = 0 when ss / cols + eps is 0;
+//   y  = fl32(fl32(x r) w), then fl32(prescale y) is quantized.
+template <int ELEM, bool VEC>
+__global__ void __launch_bounds__(256) mxq_rms_kernel(const uint16_t* __restrict__ src, int64_t nrows, int nb,
+                                                      int64_t ld, const float* __restrict__ weight, float eps,
+                                                      float prescale, bool fitmax, uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+  constexpr int BB = Fmt<ELEM>::bits * 4;
+  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = blk < nrows * nb;  // rows never straddle the end: nrows * nb is a multiple of nb
+  const int64_t row = blk / nb, g = blk - row * nb;
+  float x[32];
+  double s = 0.0;
+  if (live) {
+    const uint16_t* p = src + row * ld + g * 32;
+    if constexpr (VEC) {
+      const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = p4[i];
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[8 * i + 2 * j] = bf16_to_f32(uu[j] & 0xFFFFu);
+          x[8 * i + 2 * j + 1] = bf16_to_f32(uu[j] >> 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = bf16_to_f32(p[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s += (double)x[i] * (double)x[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+  }
+  // the row total, block sums in block order (every lane of the row alike)
+  const int lane = threadIdx.x & 63;
+  const int first = lane & ~(nb - 1);
+  double ss = 0.0;
+  for (int t = 0; t < nb; ++t) ss += __shfl(s, first + t, 64);
+  if (!live) return;
+  const double a = ss / (double)(32 * nb) + (double)eps;
+  const float r = (a == 0.0) ? 0.0f : (float)(1.0 / __builtin_sqrt(a));
+  if (weight != nullptr) {
+    float wv[32];
+    if constexpr (VEC) {
+      const float4* w4 = reinterpret_cast<const float4*>(weight + g * 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 t = w4[i];
+        wv[4 * i] = t.x; wv[4 * i + 1] = t.y; wv[4 * i + 2] = t.z; wv[4 * i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) wv[i] = weight[g * 32 + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = ((x[i] * r) * wv[i]) * prescale;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = (x[i] * r) * prescale;
+  }
+  uint32_t w[8];
+  const uint32_t code = quant_block<ELEM>(x, fitmax, w, false);
+  store_block<BB>(codes + blk * BB, w);
+  scales[blk] = (uint8_t)code;
+}
+
 // axis 1: lane (m, key block kb, column d), d fastest so a wave's loads of one
 // key row are contiguous; output row d holds the key blocks of that column.
 // Scales are written block-major with the columns interleaved:
@@ -225,6 +303,39 @@ static hipError_t launch_elem(const uint16_t* src, int64_t n_mat, int64_t rows, 
                        prescale, fitmax, codes, scales);
   }
   return hipGetLastError();
+}
+
+template <int ELEM>
+static hipError_t launch_rms_elem(const uint16_t* src, int64_t nrows, int64_t cols, int64_t ld, const float* weight,
+                                  float eps, float prescale, bool fitmax, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t stream) {
+  const int TB = 256;
+  const int nb = (int)(cols / 32);
+  const int64_t total = nrows * nb;
+  dim3 grid((unsigned)((total + TB - 1) / TB));
+  // 16-byte loads when every row start and the weight are 16-byte aligned
+  const bool vec = (ld % 8 == 0) && ((reinterpret_cast<uintptr_t>(src) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(weight) & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL((mxq_rms_kernel<ELEM, true>), grid, dim3(TB), 0, stream, src, nrows, nb, ld, weight, eps,
+                       prescale, fitmax, codes, scales);
+  else
+    hipLaunchKernelGGL((mxq_rms_kernel<ELEM, false>), grid, dim3(TB), 0, stream, src, nrows, nb, ld, weight, eps,
+                       prescale, fitmax, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mx_rmsnorm(const uint16_t* src, int64_t nrows, int64_t cols, int64_t ld,
+                                      const float* weight, float eps, float prescale, int elem, bool fitmax,
+                                      uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  switch (elem) {
+    case E4M3: return launch_rms_elem<E4M3>(src, nrows, cols, ld, weight, eps, prescale, fitmax, codes, scales, stream);
+    case E5M2: return launch_rms_elem<E5M2>(src, nrows, cols, ld, weight, eps, prescale, fitmax, codes, scales, stream);
+    case E2M3: return launch_rms_elem<E2M3>(src, nrows, cols, ld, weight, eps, prescale, fitmax, codes, scales, stream);
+    case E3M2: return launch_rms_elem<E3M2>(src, nrows, cols, ld, weight, eps, prescale, fitmax, codes, scales, stream);
+    case E2M1: return launch_rms_elem<E2M1>(src, nrows, cols, ld, weight, eps, prescale, fitmax, codes, scales, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld, int axis,

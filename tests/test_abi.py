@@ -119,3 +119,22 @@ def test_masked_forward_validation_rejects_before_launch():
     assert call(fs._Mask(1, 16, 16), _params(D=96)) == -1             # the fsattn_forward checks still apply
     assert call(fs._Mask(1, 16, 16), _params(Sq=0)) == 0              # empty: OK, no launch
     assert call(None, _params(B=0)) == 0                              # NULL mask = fsattn_forward
+
+
+def test_rmsnorm_quantize_validation():
+    R = fs.lib().fsattn_quantize_mx_rmsnorm
+    f = ctypes.c_float
+
+    def call(cols=128, ld=128, weight=None, eps=1e-6, pre=1.0, elem=2, rule=0, src=16, codes=16):
+        return R(src, 1, 4, cols, ld, weight, f(eps), f(pre), elem, rule, codes, 16, None)
+
+    assert call(cols=100, ld=100) == -1                    # cols % 32
+    assert call(ld=64) == -1                               # ld < cols
+    assert call(eps=-1.0) == -1                            # eps
+    assert call(pre=float("inf")) == -1                    # prescale
+    assert call(elem=7) == -1 and call(rule=3) == -1       # enums
+    assert call(cols=96, ld=96) == -2                      # not a power of two
+    assert call(cols=4096, ld=4096) == -2                  # beyond one wave per row
+    assert call(codes=8) == -3 and call(weight=6) == -3    # alignment
+    assert call(src=None) == -1
+    assert R(None, 0, 4, 128, 128, None, f(1e-6), f(1.0), 2, 0, None, None, None) == 0  # empty
