@@ -84,6 +84,8 @@ def lib():
         L.fso_reference.argtypes = [ctypes.POINTER(Params), ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int64, P]
         L.fso_reference_bf16.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double, P, P, P, P, ctypes.c_int64,
                                                               ctypes.c_int, P]
+        L.fso_reference_bf16_masked.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double, ctypes.POINTER(Mask), P, P, P,
+                                                                     P, ctypes.c_int64, ctypes.c_int, P]
         L.fso_folded_score.restype = ctypes.c_double
         L.fso_folded_score.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_double, ctypes.c_int]
         _lib = L
@@ -221,8 +223,10 @@ def reference(p: Params, ref: int, q, k, v, rows=None) -> np.ndarray:
     return O
 
 
-def reference_bf16(q, k, v, sigma: float, rows=None, nthreads: int = 0) -> np.ndarray:
-    """R0: exact softmax attention on bf16 inputs (uint16 arrays [B,H,S,D])."""
+def reference_bf16(q, k, v, sigma: float, rows=None, nthreads: int = 0, causal=False, q_lens=None,
+                   kv_lens=None) -> np.ndarray:
+    """R0: exact softmax attention on bf16 inputs (uint16 arrays [B,H,S,D]); with
+    causal / q_lens / kv_lens, over each row's visible keys (fso_reference_bf16_masked)."""
     q = np.ascontiguousarray(q, np.uint16)
     k = np.ascontiguousarray(k, np.uint16)
     v = np.ascontiguousarray(v, np.uint16)
@@ -231,8 +235,15 @@ def reference_bf16(q, k, v, sigma: float, rows=None, nthreads: int = 0) -> np.nd
     nrows = B * H * Sq if rows is None else len(rows)
     rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     O = np.zeros((nrows, D), np.float64)
-    rc = lib().fso_reference_bf16(B, H, Sq, Skv, D, float(sigma), _ptr(q), _ptr(k), _ptr(v), _ptr(rows_a), nrows,
-                                  nthreads, _ptr(O))
+    if causal or q_lens is not None or kv_lens is not None:
+        ql = None if q_lens is None else np.ascontiguousarray(q_lens, dtype=np.int32)
+        kl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
+        m = Mask(1 if causal else 0, _ptr(ql), _ptr(kl))
+        rc = lib().fso_reference_bf16_masked(B, H, Sq, Skv, D, float(sigma), ctypes.byref(m), _ptr(q), _ptr(k),
+                                             _ptr(v), _ptr(rows_a), nrows, nthreads, _ptr(O))
+    else:
+        rc = lib().fso_reference_bf16(B, H, Sq, Skv, D, float(sigma), _ptr(q), _ptr(k), _ptr(v), _ptr(rows_a),
+                                      nrows, nthreads, _ptr(O))
     if rc != 0:
         raise ValueError(f"fso_reference_bf16 failed ({rc})")
     return O

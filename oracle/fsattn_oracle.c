@@ -605,11 +605,11 @@ typedef struct {
 static int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 /* last key row `row` may see (-1: none), from the mask (fso_mask) */
-static int64_t last_visible_key(const fso_params* p, const fso_mask* m, int64_t row) {
-  int64_t head = row / p->Sq, b = head / p->H, i = row % p->Sq;
-  int64_t qlen = p->Sq, kvlen = p->Skv;
-  if (m && m->q_lens) qlen = clamp64(m->q_lens[b], 0, p->Sq);
-  if (m && m->kv_lens) kvlen = clamp64(m->kv_lens[b], 0, p->Skv);
+static int64_t last_visible_key(int64_t Sq, int64_t Skv, int64_t H, const fso_mask* m, int64_t row) {
+  int64_t head = row / Sq, b = head / H, i = row % Sq;
+  int64_t qlen = Sq, kvlen = Skv;
+  if (m && m->q_lens) qlen = clamp64(m->q_lens[b], 0, Sq);
+  if (m && m->kv_lens) kvlen = clamp64(m->kv_lens[b], 0, Skv);
   if (i >= qlen) return -1;
   int64_t lim = kvlen - 1;
   if (m && m->causal && i + kvlen - qlen < lim) lim = i + kvlen - qlen;
@@ -623,7 +623,7 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
   int64_t row = J->rows ? J->rows[ri] : ri;
   int64_t head = row / p->Sq;
   /* keys [0, Skv) are visible: a masked row sees a prefix of the keys */
-  int64_t Skv = last_visible_key(p, J->mask, row) + 1;
+  int64_t Skv = last_visible_key(p->Sq, p->Skv, p->H, J->mask, row) + 1;
   int qbb = fso_block_bytes(p->qk_elem);
   int bad;
   decode_row(p->qk_elem, J->qc + (row * nbd) * qbb, J->qs + row * nbd, D, rb->qm, rb->qe, &bad);
@@ -920,6 +920,7 @@ typedef struct {
   const int64_t* rows;
   int64_t nrows;
   double* O;
+  const fso_mask* mask; /* NULL: no mask */
   int64_t next;
   pthread_mutex_t mu;
 } r0_t;
@@ -939,18 +940,21 @@ static void* r0_worker(void* arg) {
     int64_t head = row / R->Sq;
     const uint16_t* qr = R->q + row * D;
     for (int d = 0; d < D; ++d) qd[d] = bf16_to_double(qr[d]);
+    /* keys [0, nvis) are visible (the mask of fso_forward_masked) */
+    const int64_t nvis = last_visible_key(R->Sq, R->Skv, R->H, R->mask, row) + 1;
+    double* O = R->O + ri * D;
+    for (int d = 0; d < D; ++d) O[d] = 0.0;
+    if (nvis == 0) continue;
     double m = -INFINITY;
-    for (int64_t k = 0; k < R->Skv; ++k) {
+    for (int64_t k = 0; k < nvis; ++k) {
       const uint16_t* kr = R->k + (head * R->Skv + k) * D;
       double acc = 0.0;
       for (int d = 0; d < D; ++d) acc += qd[d] * bf16_to_double(kr[d]);
       s[k] = acc * R->sigma;
       if (s[k] > m) m = s[k];
     }
-    double* O = R->O + ri * D;
-    for (int d = 0; d < D; ++d) O[d] = 0.0;
     double l = 0.0;
-    for (int64_t k = 0; k < R->Skv; ++k) {
+    for (int64_t k = 0; k < nvis; ++k) {
       double pk = exp(s[k] - m);
       const uint16_t* vr = R->v + (head * R->Skv + k) * D;
       for (int d = 0; d < D; ++d) O[d] += pk * bf16_to_double(vr[d]);
@@ -965,6 +969,12 @@ static void* r0_worker(void* arg) {
 
 int fso_reference_bf16(int B, int H, int Sq, int Skv, int D, double sigma, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, const int64_t* rows, int64_t nrows, int nthreads, double* out_O) {
+  return fso_reference_bf16_masked(B, H, Sq, Skv, D, sigma, NULL, q, k, v, rows, nrows, nthreads, out_O);
+}
+
+int fso_reference_bf16_masked(int B, int H, int Sq, int Skv, int D, double sigma, const fso_mask* mask,
+                              const uint16_t* q, const uint16_t* k, const uint16_t* v, const int64_t* rows,
+                              int64_t nrows, int nthreads, double* out_O) {
   if (B < 0 || H < 0 || Sq < 0 || Skv < 1 || D < 1) return FSO_EINVAL;
   int64_t total = (int64_t)B * H * Sq;
   if (!rows) nrows = total;
@@ -972,7 +982,7 @@ int fso_reference_bf16(int B, int H, int Sq, int Skv, int D, double sigma, const
     if (rows[i] < 0 || rows[i] >= total) return FSO_EINVAL;
   r0_t R;
   R.B = B; R.H = H; R.Sq = Sq; R.Skv = Skv; R.D = D; R.sigma = sigma; R.q = q; R.k = k; R.v = v;
-  R.rows = rows; R.nrows = nrows; R.O = out_O; R.next = 0;
+  R.rows = rows; R.nrows = nrows; R.O = out_O; R.mask = mask; R.next = 0;
   pthread_mutex_init(&R.mu, NULL);
   int nt = nthreads > 0 ? nthreads : fso_default_threads();
   if (nt > nrows) nt = (int)(nrows > 0 ? nrows : 1);

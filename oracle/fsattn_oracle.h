@@ -176,6 +176,12 @@ int fso_reference_bf16(int B, int H, int Sq, int Skv, int D, double sigma,
                        const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int64_t* rows, int64_t nrows, int nthreads, double* out_O);
 
+/* R0 under the mask of fso_forward_masked: row i's softmax runs over its
+ * visible keys only; a row that sees no key (or i >= q_len) is 0. */
+int fso_reference_bf16_masked(int B, int H, int Sq, int Skv, int D, double sigma, const fso_mask* mask,
+                              const uint16_t* q, const uint16_t* k, const uint16_t* v, const int64_t* rows,
+                              int64_t nrows, int nthreads, double* out_O);
+
 /* Exact folded score of one (query,key) pair: returns fl32(cinit + sum_d qhat*khat),
  * or the double value when exact_fold != 0.  Exposed for the pins. */
 double fso_folded_score(int qk_elem, const uint8_t* qrow_codes, const uint8_t* qrow_scales,

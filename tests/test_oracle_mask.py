@@ -201,3 +201,28 @@ def test_qlen_rows_zero_and_full_mask_is_identity(oracle):
     a = oracle.forward(p1, Q1, K1, V1)
     c = oracle.forward(p1, Q1, K1, V1, causal=True)
     assert np.array_equal(a["O"], c["O"])
+
+
+@pytest.mark.parametrize("Sq,Skv", [(40, 40), (25, 90), (60, 30)])
+def test_masked_r0_is_prefix_softmax(oracle, Sq, Skv):
+    """R0 under a causal mask and key lengths: row i equals the unmasked R0 of
+    the one-query problem on its visible keys; rows that see nothing are 0."""
+    B, H, D = 2, 1, 32
+    q = bits(rand_bf16((B, H, Sq, D), 51))
+    k = bits(rand_bf16((B, H, Skv, D), 52))
+    v = bits(rand_bf16((B, H, Skv, D), 53))
+    kv_lens = [Skv, max(1, Skv // 2)]
+    q_lens = [Sq, Sq - 3]
+    sigma = 0.2
+    R = oracle.reference_bf16(q, k, v, sigma, causal=True, q_lens=q_lens, kv_lens=kv_lens)
+    for b in range(B):
+        vis = visible_counts(Sq, Skv, True, q_lens[b], kv_lens[b])
+        for i in range(Sq):
+            row = R[b * Sq + i]
+            if vis[i] == 0:
+                assert not row.any()
+                continue
+            n = int(vis[i])
+            ref = oracle.reference_bf16(q[b:b + 1, :, i:i + 1].copy(), k[b:b + 1, :, :n].copy(),
+                                        v[b:b + 1, :, :n].copy(), sigma)
+            assert np.array_equal(row, ref[0]), (b, i)
