@@ -177,18 +177,18 @@ def time_prologue(fs, w, q, k, steps):
     return res
 
 
-def time_bf16(fs, w, q, k, v, steps, warmup):
+def time_bf16(fs, w, q, k, v, steps, warmup, causal=False):
     import torch
 
     st = torch.cuda.current_stream()
     out = torch.empty_like(q)
     for _ in range(warmup):
-        fs.forward_bf16_baseline(q, k, v, w.sigma, out=out)
+        fs.forward_bf16_baseline(q, k, v, w.sigma, out=out, causal=causal)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in ev:
         a.record(st)
-        fs.forward_bf16_baseline(q, k, v, w.sigma, out=out)
+        fs.forward_bf16_baseline(q, k, v, w.sigma, out=out, causal=causal)
         b.record(st)
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) for a, b in ev]
@@ -312,6 +312,11 @@ def main():
                                        "mx_mfma_util": round(c_tf / _peak_for(w), 4), "rollbacks": c_cnt,
                                        "flops": c_flops,
                                        "time_vs_unmasked": round(c_ms / main_res[1], 4)}
+        if not args.no_bf16:
+            print("[bench] bf16 baseline causal", file=sys.stderr, flush=True)
+            cb_ms, _ = time_bf16(fs, w, q, k, v, max(3, args.steps // 2), 1, causal=True)
+            formats[w.name + "-causal"]["bf16_causal_kernel_ms"] = round(cb_ms, 4)
+            formats[w.name + "-causal"]["speedup_vs_bf16_causal_kernel"] = round(cb_ms / c_ms, 3)
 
     if not args.no_prologue and w.name.startswith("video-"):
         print("[bench] fused prologue", file=sys.stderr, flush=True)

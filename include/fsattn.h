@@ -236,6 +236,21 @@ int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const
 int fsattn_forward_bf16_baseline(const void* q, const void* k, const void* v, int B, int H, int Sq, int Skv,
                                  int D, float softmax_scale, void* out, void* stream);
 
+/*
+ * fsattn_forward_bf16_baseline_masked -- the BF16 baseline under the masks of
+ * fsattn_forward_masked (causal, per-batch device q_lens / kv_lens; mask NULL
+ * = fsattn_forward_bf16_baseline): each row's softmax runs over its visible
+ * keys; rows that see no key, and rows past q_len, are stored as 0.  The
+ * comparison point for masked fused attention (masks precede the softmax,
+ * "Fused softmax makes quantized attention faster on AMD GPUs", section "What
+ * the evidence shows").  Errors as fsattn_forward_bf16_baseline, plus
+ * FSATTN_E_INVALID_ARG if causal is not 0/1 and FSATTN_E_ALIGNMENT if a
+ * length array is not 4-byte aligned.
+ */
+int fsattn_forward_bf16_baseline_masked(const void* q, const void* k, const void* v, int B, int H, int Sq, int Skv,
+                                        int D, float softmax_scale, const fsattn_mask* mask, void* out,
+                                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ SCALE_FITMAX, SCALE_OCP_FLOOR = 0, 1
 ABI_SYMBOLS = (
     "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
     "fsattn_quantize_mx", "fsattn_quantize_mx_rmsnorm", "fsattn_forward", "fsattn_forward_masked",
-    "fsattn_forward_bf16_baseline",
+    "fsattn_forward_bf16_baseline", "fsattn_forward_bf16_baseline_masked",
 )
 
 
@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(_MxTensor), V, V]
         L.fsattn_forward_bf16_baseline.restype = I
         L.fsattn_forward_bf16_baseline.argtypes = [V, V, V, I, I, I, I, I, ctypes.c_float, V, V]
+        L.fsattn_forward_bf16_baseline_masked.restype = I
+        L.fsattn_forward_bf16_baseline_masked.argtypes = [V, V, V, I, I, I, I, I, ctypes.c_float,
+                                                          ctypes.POINTER(_Mask), V, V]
         _lib = L
     return _lib
 
@@ -227,12 +230,26 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
 
 
 def forward_bf16_baseline(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float,
-                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Conventional BF16 attention forward (online softmax).  q [B,H,Sq,D], k/v [B,H,Skv,D]."""
+                          out: torch.Tensor | None = None, stream=None, causal: bool = False,
+                          q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None) -> torch.Tensor:
+    """Conventional BF16 attention forward (online softmax).  q [B,H,Sq,D], k/v [B,H,Skv,D].
+    causal / q_lens / kv_lens: the masks of forward() (fsattn_forward_bf16_baseline_masked)."""
     B, H, Sq, D = q.shape
     Skv = k.shape[2]
     if out is None:
         out = torch.empty_like(q)
+    if causal or q_lens is not None or kv_lens is not None:
+        for t in (q_lens, kv_lens):
+            if t is not None and (t.dtype != torch.int32 or t.device != q.device or t.shape != (B,) or
+                                  not t.is_contiguous()):
+                raise ValueError("q_lens / kv_lens must be contiguous int32 [B] on the inputs' device")
+        m = _Mask(1 if causal else 0, q_lens.data_ptr() if q_lens is not None else None,
+                  kv_lens.data_ptr() if kv_lens is not None else None)
+        st = lib().fsattn_forward_bf16_baseline_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Sq, Skv, D,
+                                                       ctypes.c_float(softmax_scale), ctypes.byref(m),
+                                                       out.data_ptr(), _stream(stream))
+        _check("fsattn_forward_bf16_baseline_masked", st)
+        return out
     st = lib().fsattn_forward_bf16_baseline(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Sq, Skv, D,
                                             ctypes.c_float(softmax_scale), out.data_ptr(), _stream(stream))
     _check("fsattn_forward_bf16_baseline", st)

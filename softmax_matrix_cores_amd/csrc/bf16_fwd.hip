@@ -76,7 +76,9 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                uint16_t* __restrict__ out, int H, int Sq, int Skv,
-                                                               float c_log2) {
+                                                               float c_log2, int causal,
+                                                               const int32_t* __restrict__ q_lens,
+                                                               const int32_t* __restrict__ kv_lens) {
   using G = BGeo<D>;
   constexpr int NO = G::NO, NC = G::NC;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
@@ -85,9 +87,35 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const int bh = blockIdx.y + blockIdx.z * H;
-  const int qw0 = blockIdx.x * BQG + w * BQ;
-  const int ns = (Skv + BK - 1) / BK;
-  const int nklast = Skv - (ns - 1) * BK;
+  // masks as for the fused forward: valid queries / keys of the batch, and the
+  // causal limit k <= i + kv_len - q_len; causal workgroups longest first
+  const int q_len = q_lens ? min(max(q_lens[blockIdx.z], 0), Sq) : Sq;
+  const int kv_len = kv_lens ? min(max(kv_lens[blockIdx.z], 0), Skv) : Skv;
+  const int coff = kv_len - q_len;
+  const int q0 = (causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x) * BQG;
+  const int qw0 = q0 + w * BQ;
+  int kend = q0 < q_len ? kv_len : 0;  // keys [0, kend) are read
+  if (causal) kend = max(min(kend, min(q0 + BQG, q_len) + coff), 0);
+  const int ns = (kend + BK - 1) / BK;
+  // keys [0, lim) visible to this lane's query; steps from ums on hold a
+  // masked key for some row of the wave
+  const int lim = (causal && qw0 + n < q_len) ? min(kend, qw0 + n + coff + 1) : kend;
+  const int lim_w = (causal && qw0 < q_len) ? min(kend, qw0 + coff + 1) : kend;
+  const int ums = max(lim_w, 0) / BK;
+  if (ns == 0) {
+    // no visible key in the workgroup (uniform): zero rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qq = qw0 + 8 * i + 4 * hh + j;
+        if (qq < Sq) {
+#pragma unroll
+          for (int o = 0; o < NO; ++o) out[((size_t)bh * Sq + qq) * D + 32 * o + n] = 0;
+        }
+      }
+    return;
+  }
 
   // ---- DMA plan: wave w issues loads 4 (w & 3) .. 4 (w & 3) + PER_WAVE - 1 of
   // its side every step, at constant per-lane offsets
@@ -108,7 +136,7 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
     }
   }
   const uint64_t base = (uint64_t)(uintptr_t)((kside ? k : v) + (size_t)bh * Skv * D);
-  int rem = Skv * G::ROW;
+  int rem = kend * G::ROW;
   const int stride = BK * G::ROW;
   v4i rc = rsrc(base, rem);
   auto advance = [&]() {
@@ -214,14 +242,15 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
       }
     }
     // lane (q, h), register 4i + j of key group kg holds key 32 kg + 16(i/2) + 8h + 4(i%2) + j
-    if (u == ns - 1 && nklast < BK) {
+    if (u >= ums) {
+      const int nk = lim - u * BK;  // this lane's visible keys of the step
 #pragma unroll
       for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int i = e >> 2, j = e & 3;
           const int key = 32 * kg + 16 * (i >> 1) + 8 * hh + 4 * (i & 1) + j;
-          if (key >= nklast) S[kg][e] = -INFINITY;
+          if (key >= nk) S[kg][e] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -248,14 +277,16 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
         }
       m = mnew;
     }
-    // p = exp2(s c - m), l += p, P operands of the four 16-key chunks
+    // p = exp2(s c - m), l += p, P operands of the four 16-key chunks (a row
+    // that has seen no key yet keeps m = -inf: its masked scores give p = 0)
+    const float mref = m > -INFINITY ? m : 0.0f;
     uint32_t pw[16];
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kg][e], c_log2, -m));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kg][e + 1], c_log2, -m));
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kg][e], c_log2, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kg][e + 1], c_log2, -mref));
         lsum += p0 + p1;
         pw[8 * kg + e / 2] = pk_bf16(p0, p1);
       }
@@ -285,11 +316,13 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
       const float lq = __shfl(ltot, qi, 64);
       const int qq = qw0 + qi;
       if (qq < Sq) {
-        const float inv = 1.0f / lq;
+        // rows past q_len and rows that saw no key are stored as 0
+        const bool live = qq < q_len && lq > 0.0f;
+        const float inv = live ? 1.0f / lq : 0.0f;
         uint16_t* orow = out + ((size_t)bh * Sq + qq) * D;
 #pragma unroll
         for (int o = 0; o < NO; ++o) {
-          uint32_t uo = __float_as_uint(O[o][4 * i + j] * inv);
+          uint32_t uo = live ? __float_as_uint(O[o][4 * i + j] * inv) : 0u;
           uo = (uo + 0x7FFFu + ((uo >> 16) & 1u)) >> 16;  // RNE to bf16 (finite values)
           orow[32 * o + n] = (uint16_t)uo;
         }
@@ -300,13 +333,16 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
 }  // namespace
 
 hipError_t launch_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int B, int H,
-                           int Sq, int Skv, int D, float softmax_scale, hipStream_t stream) {
+                           int Sq, int Skv, int D, float softmax_scale, int causal, const int32_t* q_lens,
+                           const int32_t* kv_lens, hipStream_t stream) {
   const float c_log2 = softmax_scale * 1.4426950408889634f;
   dim3 grid((unsigned)((Sq + BQG - 1) / BQG), (unsigned)H, (unsigned)B);
   if (D == 128)
-    hipLaunchKernelGGL(bf16_fwd_kernel<128>, grid, dim3(BW * 64), 0, stream, q, k, v, out, H, Sq, Skv, c_log2);
+    hipLaunchKernelGGL(bf16_fwd_kernel<128>, grid, dim3(BW * 64), 0, stream, q, k, v, out, H, Sq, Skv, c_log2,
+                       causal, q_lens, kv_lens);
   else
-    hipLaunchKernelGGL(bf16_fwd_kernel<64>, grid, dim3(BW * 64), 0, stream, q, k, v, out, H, Sq, Skv, c_log2);
+    hipLaunchKernelGGL(bf16_fwd_kernel<64>, grid, dim3(BW * 64), 0, stream, q, k, v, out, H, Sq, Skv, c_log2,
+                       causal, q_lens, kv_lens);
   return hipGetLastError();
 }
 

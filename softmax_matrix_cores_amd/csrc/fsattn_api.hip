@@ -184,6 +184,16 @@ int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsat
 
 int fsattn_forward_bf16_baseline(const void* q, const void* k, const void* v, int B, int H, int Sq, int Skv, int D,
                                  float softmax_scale, void* out, void* stream) {
+  return fsattn_forward_bf16_baseline_masked(q, k, v, B, H, Sq, Skv, D, softmax_scale, nullptr, out, stream);
+}
+
+int fsattn_forward_bf16_baseline_masked(const void* q, const void* k, const void* v, int B, int H, int Sq, int Skv,
+                                        int D, float softmax_scale, const fsattn_mask* mask, void* out,
+                                        void* stream) {
+  if (mask) {
+    if (mask->causal != 0 && mask->causal != 1) return FSATTN_E_INVALID_ARG;
+    if (!aligned(mask->q_lens, 4) || !aligned(mask->kv_lens, 4)) return FSATTN_E_ALIGNMENT;
+  }
   if (B < 0 || H < 0 || Sq < 0 || Skv < 1 || (D != 64 && D != 128)) return FSATTN_E_INVALID_ARG;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FSATTN_E_INVALID_ARG;
   if (H > 65535 || B > 65535) return FSATTN_E_UNSUPPORTED;
@@ -192,7 +202,8 @@ int fsattn_forward_bf16_baseline(const void* q, const void* k, const void* v, in
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4)) return FSATTN_E_ALIGNMENT;
   hipError_t e = fsattn::launch_bf16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), B, H, Sq, Skv,
-                                         D, softmax_scale, static_cast<hipStream_t>(stream));
+                                         D, softmax_scale, mask ? mask->causal : 0, mask ? mask->q_lens : nullptr,
+                                         mask ? mask->kv_lens : nullptr, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
 }
 

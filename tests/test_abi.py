@@ -138,3 +138,13 @@ def test_rmsnorm_quantize_validation():
     assert call(codes=8) == -3 and call(weight=6) == -3    # alignment
     assert call(src=None) == -1
     assert R(None, 0, 4, 128, 128, None, f(1e-6), f(1.0), 2, 0, None, None, None) == 0  # empty
+
+
+def test_bf16_masked_validation():
+    B = fs.lib().fsattn_forward_bf16_baseline_masked
+    f = ctypes.c_float(0.1)
+    assert B(16, 16, 16, 1, 1, 8, 8, 128, f, ctypes.byref(fs._Mask(2, None, None)), 16, None) == -1
+    assert B(16, 16, 16, 1, 1, 8, 8, 128, f, ctypes.byref(fs._Mask(1, 2, None)), 16, None) == -3
+    assert B(16, 16, 16, 1, 1, 8, 8, 96, f, ctypes.byref(fs._Mask(1, None, None)), 16, None) == -1
+    assert B(16, 16, 16, 1, 1, 0, 8, 128, f, ctypes.byref(fs._Mask(1, 16, 16)), 16, None) == 0
+    assert B(16, 16, 16, 1, 1, 0, 8, 128, f, None, 16, None) == 0

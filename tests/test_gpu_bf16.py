@@ -45,3 +45,32 @@ def test_bf16_full_size_sampled(oracle, name):
     err = rel_frob(g.astype(np.float64), R0)
     log(f"[case] bf16 {name}: rel_frob={err:.3e}")
     assert err <= 1e-2
+
+
+MASKED = [
+    # name, base, sizes, causal, q_lens, kv_lens
+    ("bf16-causal-square", "qknorm-mxfp6", dict(B=1, H=2, Sq=300, Skv=300, D=128, seed=41), True, None, None),
+    ("bf16-causal-q<kv", "tiny-mxfp8", dict(B=1, H=2, Sq=90, Skv=410, D=64, seed=42), True, None, None),
+    ("bf16-causal-q>kv", "qknorm-mxfp6", dict(B=1, H=1, Sq=290, Skv=120, D=128, seed=43), True, None, None),
+    ("bf16-varlen-causal", "qknorm-mxfp6", dict(B=3, H=1, Sq=260, Skv=300, D=128, seed=44), True, [260, 100, 7],
+     [300, 65, 0]),
+]
+
+
+@pytest.mark.parametrize("name,base,kw,causal,q_lens,kv_lens", MASKED, ids=[c[0] for c in MASKED])
+def test_bf16_masked(oracle, name, base, kw, causal, q_lens, kv_lens):
+    w = W.custom(base, name=name, **kw)
+    log(f"[case] {name}")
+    q, k, v = W.make_inputs(w, device="cuda:0")
+    dev = q.device
+    ql = None if q_lens is None else torch.tensor(q_lens, dtype=torch.int32, device=dev)
+    kl = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device=dev)
+    out = fs.forward_bf16_baseline(q, k, v, w.sigma, causal=causal, q_lens=ql, kv_lens=kl)
+    torch.cuda.synchronize()
+    R0 = oracle.reference_bf16(bits(q), bits(k), bits(v), w.sigma, causal=causal, q_lens=q_lens, kv_lens=kv_lens)
+    g = out.float().cpu().numpy().reshape(-1, w.D).astype(np.float64)
+    err = rel_frob(g, R0)
+    dead = ~R0.any(axis=1)
+    log(f"[case] {name}: rel_frob={err:.3e} dead_rows={int(dead.sum())}")
+    assert err <= 1e-2
+    assert not g[dead].any()

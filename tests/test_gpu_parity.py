@@ -29,6 +29,7 @@ SMALL = [
                                         v_elem="e2m1", p_elem="e2m3")),
     ("fp6-skv1", "qknorm-mxfp6", dict(B=1, H=1, Sq=33, Skv=1, D=128, seed=18)),
     ("fp8-skv40", "tiny-mxfp8", dict(B=1, H=1, Sq=20, Skv=40, D=128, seed=19)),
+    ("fp6-sq1", "qknorm-mxfp6", dict(B=1, H=3, Sq=1, Skv=700, D=128, seed=20)),
 ]
 
 
