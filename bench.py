@@ -52,7 +52,15 @@ def _peak_for(w) -> float:
 
 
 def _src_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and blank lines removed, so that
+    a comment edit does not retire a traffic measurement of the same code."""
+    import re
+
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def _traffic(workload: str):

@@ -43,8 +43,16 @@
 //     half a max3.  The E8M0 of P comes from the block max with integer
 //     exponent arithmetic; one v_cvt_scalef32_pk32_fp6_bf16 converts a lane's
 //     32 keys.  A wave ballot sends a step to the exact path on the first
-//     step, a partial last step, a possible gate fire or stage-1 clamp, or a
-//     block low enough that the BF16 subnormal flush could change a code.
+//     step, a step holding a masked key (past the batch's key count, or past
+//     a row's causal limit), a possible gate fire or stage-1 clamp, or a
+//     block low enough that the BF16 subnormal flush could change a code.  A
+//     step whose only issue is a gate fire takes a shorter path: the shift,
+//     then the fast conversion again.  A fire updates the C splat in place,
+//     and FP6 P lives in six registers, so that the fast path carries no
+//     register copies between steps.
+//   * masks (causal, per-batch query / key counts): a workgroup reads only
+//     the keys its valid queries see; causal workgroups start longest first;
+//     rows that see no key, and rows past the query count, are stored as 0.
 //   * a 128-key gate tile spans two steps: on the even step the scores of the
 //     odd step are computed once ahead of time for their maximum only, and
 //     computed again (with the gate's new offset) on the odd step.
