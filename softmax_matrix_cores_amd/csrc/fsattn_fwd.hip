@@ -827,6 +827,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     sync();
     KOps kop;
     if constexpr (PRE_K) kop = read_k(u + 1);
+    // the PV products and the conversion run at raised wave priority: when
+    // both waves of a SIMD can issue, the one feeding the matrix core while
+    // converting goes first (the rest of the step runs at the normal level)
+    __builtin_amdgcn_s_setprio(3);
     if constexpr (PRE_V) pv_of(pA, pS, vop);
     else pv_of(pA, pS, read_v(u - 1));
     const Check c = check(S, u, mn);
@@ -850,6 +854,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     }
     pA = pAf;
     pS = pSf;
+    __builtin_amdgcn_s_setprio(0);
     if (rare) {
       bool done = false;
       if constexpr (!KV128 && !Opd<PE>::split) done = u < ums && gate_fast(S, c, dsc);
