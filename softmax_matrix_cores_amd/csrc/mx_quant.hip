@@ -281,6 +281,57 @@ __global__ void __launch_bounds__(256) mxq_axis1_kernel(const uint16_t* __restri
   scales[((m * nb + kb) * 32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)code;
 }
 
+// axis 1, tiled (cols 64 or 128, 16-byte rows): a workgroup quantizes keys
+// [256 t, 256 t + 256) of every column of matrix m.  The bf16 tile comes in
+// with 16-byte coalesced loads; in LDS each 16-byte chunk of row r sits
+// rotated by 8 ((r / 32) % 8) columns (mod cols), so that the column reads
+// below (lanes = 8 key blocks x 8 columns) hit 32 distinct banks.  Each thread
+// then quantizes (column, 32-key block) units with the key block fastest, so
+// neighbouring threads write neighbouring blocks of one column: the packed
+// codes leave as contiguous runs.  The arithmetic per block is the same as
+// mxq_axis1_kernel's (same quant_block, zero padding past the last key).
+constexpr int AX1_KT = 256;  // keys per tile
+template <int ELEM, int COLS>
+__global__ void __launch_bounds__(256) mxq_axis1_tiled_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                              int64_t ld, int64_t nb, float prescale, bool fitmax,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+  constexpr int BB = Fmt<ELEM>::bits * 4;
+  constexpr int NBT = AX1_KT / 32;  // key blocks per tile
+  constexpr int CPR = COLS / 8;     // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint16_t tile[AX1_KT * COLS];
+  const int64_t m = blockIdx.y;
+  const int64_t r0 = (int64_t)blockIdx.x * AX1_KT;
+  const int rows_t = (int)min((int64_t)AX1_KT, rows - r0);  // >= 1
+  const uint16_t* base = src + (m * rows + r0) * ld;
+  for (int c = threadIdx.x; c < AX1_KT * CPR; c += 256) {
+    const int r = c / CPR, q = c - r * CPR;
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows_t) u = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + 8 * q);
+    const int col = (8 * q + 8 * ((r >> 5) & 7)) & (COLS - 1);
+    *reinterpret_cast<uint4*>(tile + r * COLS + col) = u;
+  }
+  __syncthreads();
+  const int nbt = (rows_t + 31) / 32;
+  for (int u = threadIdx.x; u < NBT * COLS; u += 256) {
+    const int kb = u % NBT, d = u / NBT;
+    if (kb >= nbt) continue;
+    const int col = (d + 8 * (kb & 7)) & (COLS - 1);
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int r = kb * 32 + j;
+      x[j] = (r < rows_t) ? bf16_to_f32(tile[r * COLS + col]) * prescale : 0.0f;
+    }
+    uint32_t w[8];
+    const uint32_t code = quant_block<ELEM>(x, fitmax, w, prescale == 1.0f);
+    const int64_t kbg = (int64_t)blockIdx.x * NBT + kb;
+    const int64_t o = (m * COLS + d) * nb + kbg;
+    store_block<BB>(codes + o * BB, w);
+    scales[((m * nb + kbg) * 32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)code;
+  }
+}
+
 template <int ELEM>
 static hipError_t launch_elem(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld,
                               int axis, float prescale, bool fitmax, uint8_t* codes, uint8_t* scales,
@@ -298,9 +349,21 @@ static hipError_t launch_elem(const uint16_t* src, int64_t n_mat, int64_t rows, 
                          prescale, fitmax, codes, scales);
   } else {
     int64_t nb = (rows + 31) / 32, total = n_mat * nb * cols;
-    dim3 grid((unsigned)((total + TB - 1) / TB));
-    hipLaunchKernelGGL((mxq_axis1_kernel<ELEM>), grid, dim3(TB), 0, stream, src, n_mat, rows, cols, ld, nb,
-                       prescale, fitmax, codes, scales);
+    const bool tiled = (cols == 64 || cols == 128) && (ld % 8 == 0) &&
+                       ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && n_mat <= 65535;
+    if (tiled) {
+      dim3 grid((unsigned)((rows + AX1_KT - 1) / AX1_KT), (unsigned)n_mat);
+      if (cols == 128)
+        hipLaunchKernelGGL((mxq_axis1_tiled_kernel<ELEM, 128>), grid, dim3(TB), 0, stream, src, rows, ld, nb,
+                           prescale, fitmax, codes, scales);
+      else
+        hipLaunchKernelGGL((mxq_axis1_tiled_kernel<ELEM, 64>), grid, dim3(TB), 0, stream, src, rows, ld, nb,
+                           prescale, fitmax, codes, scales);
+    } else {
+      dim3 grid((unsigned)((total + TB - 1) / TB));
+      hipLaunchKernelGGL((mxq_axis1_kernel<ELEM>), grid, dim3(TB), 0, stream, src, n_mat, rows, cols, ld, nb,
+                         prescale, fitmax, codes, scales);
+    }
   }
   return hipGetLastError();
 }
