@@ -282,15 +282,16 @@ __global__ void __launch_bounds__(256) mxq_axis1_kernel(const uint16_t* __restri
 }
 
 // axis 1, tiled (cols 64 or 128, 16-byte rows): a workgroup quantizes keys
-// [256 t, 256 t + 256) of every column of matrix m.  The bf16 tile comes in
-// with 16-byte coalesced loads; in LDS each 16-byte chunk of row r sits
-// rotated by 8 ((r / 32) % 8) columns (mod cols), so that the column reads
-// below (lanes = 8 key blocks x 8 columns) hit 32 distinct banks.  Each thread
+// [128 t, 128 t + 128) of every column of matrix m.  The bf16 tile (32 KiB at
+// most, so four workgroups share a CU's LDS) comes in with 16-byte coalesced
+// loads; in LDS each 16-byte chunk of row r sits rotated by 16 ((r / 32) % 4)
+// columns (mod cols), so that the column reads below (lanes = 4 key blocks x
+// 16 columns) hit 32 distinct banks.  Each thread
 // then quantizes (column, 32-key block) units with the key block fastest, so
 // neighbouring threads write neighbouring blocks of one column: the packed
 // codes leave as contiguous runs.  The arithmetic per block is the same as
 // mxq_axis1_kernel's (same quant_block, zero padding past the last key).
-constexpr int AX1_KT = 256;  // keys per tile
+constexpr int AX1_KT = 128;  // keys per tile
 template <int ELEM, int COLS>
 __global__ void __launch_bounds__(256) mxq_axis1_tiled_kernel(const uint16_t* __restrict__ src, int64_t rows,
                                                               int64_t ld, int64_t nb, float prescale, bool fitmax,
@@ -299,6 +300,7 @@ __global__ void __launch_bounds__(256) mxq_axis1_tiled_kernel(const uint16_t* __
   constexpr int BB = Fmt<ELEM>::bits * 4;
   constexpr int NBT = AX1_KT / 32;  // key blocks per tile
   constexpr int CPR = COLS / 8;     // 16-byte chunks per row
+  constexpr int ROT = 64 / NBT;     // rotation step (columns) per key block
   __shared__ __attribute__((aligned(16))) uint16_t tile[AX1_KT * COLS];
   const int64_t m = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * AX1_KT;
@@ -308,7 +310,7 @@ __global__ void __launch_bounds__(256) mxq_axis1_tiled_kernel(const uint16_t* __
     const int r = c / CPR, q = c - r * CPR;
     uint4 u = make_uint4(0u, 0u, 0u, 0u);
     if (r < rows_t) u = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + 8 * q);
-    const int col = (8 * q + 8 * ((r >> 5) & 7)) & (COLS - 1);
+    const int col = (8 * q + ROT * ((r >> 5) & (NBT - 1))) & (COLS - 1);
     *reinterpret_cast<uint4*>(tile + r * COLS + col) = u;
   }
   __syncthreads();
@@ -316,7 +318,7 @@ __global__ void __launch_bounds__(256) mxq_axis1_tiled_kernel(const uint16_t* __
   for (int u = threadIdx.x; u < NBT * COLS; u += 256) {
     const int kb = u % NBT, d = u / NBT;
     if (kb >= nbt) continue;
-    const int col = (d + 8 * (kb & 7)) & (COLS - 1);
+    const int col = (d + ROT * kb) & (COLS - 1);
     float x[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
