@@ -25,7 +25,7 @@ E4M3, E5M2, E2M3, E3M2, E2M1 = 0, 1, 2, 3, 4
 ELEM_NAMES = {"e4m3": E4M3, "e5m2": E5M2, "e2m3": E2M3, "e3m2": E3M2, "e2m1": E2M1}
 SCALE_FITMAX, SCALE_OCP_FLOOR = 0, 1
 EXP_SCHRAUDOLPH, EXP_EXACT = 0, 1
-P_MX, P_NONE = 0, 1
+P_MX, P_NONE, P_EFQ = 0, 1, 2
 FOLD_FP32, FOLD_EXACT = 0, 1
 REF_R1, REF_R2, REF_R2P, REF_R3 = 1, 2, 3, 4
 
@@ -46,7 +46,7 @@ class Params(ctypes.Structure):
         ("qk_elem", ctypes.c_int), ("v_elem", ctypes.c_int), ("p_elem", ctypes.c_int), ("scale_rule", ctypes.c_int),
         ("tau", ctypes.c_double), ("c", ctypes.c_double), ("kv_tile", ctypes.c_int),
         ("exp_mode", ctypes.c_int), ("p_mode", ctypes.c_int), ("fold_mode", ctypes.c_int),
-        ("nthreads", ctypes.c_int),
+        ("nthreads", ctypes.c_int), ("efq_tau", ctypes.c_double), ("efq_h", ctypes.c_double),
     ]
 
 
@@ -78,6 +78,7 @@ def lib():
                                               P, ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, P, P]
         L.fso_stage1.restype = ctypes.c_uint16
         L.fso_stage1.argtypes = [ctypes.c_float]
+        L.fso_efq_block.argtypes = [P, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_double, P, P]
         L.fso_forward.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P, ctypes.c_int64, P, P, P, P, P]
         L.fso_forward_masked.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Mask), P, P, P, P, P, P, P,
                                          ctypes.c_int64, P, P, P, P, P]
@@ -174,9 +175,24 @@ def quantize_mx_rmsnorm(x_bf16: np.ndarray, elem: int, prescale: float = 1.0, we
 
 
 def make_params(B, H, Sq, Skv, D, qk_elem, v_elem, p_elem, tau=8.0, c=0.0, kv_tile=64, scale_rule=SCALE_FITMAX,
-                exp_mode=EXP_SCHRAUDOLPH, p_mode=P_MX, fold_mode=FOLD_FP32, nthreads=0) -> Params:
+                exp_mode=EXP_SCHRAUDOLPH, p_mode=P_MX, fold_mode=FOLD_FP32, nthreads=0, efq_tau=0.0,
+                efq_h=0.5) -> Params:
     return Params(B, H, Sq, Skv, D, qk_elem, v_elem, p_elem, scale_rule, float(tau), float(c), kv_tile,
-                  exp_mode, p_mode, fold_mode, nthreads)
+                  exp_mode, p_mode, fold_mode, nthreads, float(efq_tau), float(efq_h))
+
+
+def efq_block(t, T0: float, tau: float, h: float, nvis: int | None = None):
+    """R24 on one block: t = up to 32 folded binary32 scores (keys past nvis
+    absent).  Returns (codes uint8[32], E8M0 int)."""
+    tf = np.zeros(32, np.float32)
+    t = np.asarray(t, np.float32)
+    tf[:len(t)] = t
+    n = len(t) if nvis is None else nvis
+    codes = np.zeros(32, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    lib().fso_efq_block(_ptr(tf), int(n), ctypes.c_float(T0), ctypes.c_double(tau), ctypes.c_double(h), _ptr(codes),
+                        _ptr(sc))
+    return codes, int(sc[0])
 
 
 def forward(p: Params, q, k, v, rows=None, want_p=False, causal=False, q_lens=None, kv_lens=None):

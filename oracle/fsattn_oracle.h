@@ -48,7 +48,7 @@ enum { FSO_SCALE_FITMAX = 0, FSO_SCALE_OCP_FLOOR = 1 };
 /* switches used by the invariant checks; the method itself is
  * exp=SCHRAUDOLPH, p=MX, fold=FP32 */
 enum { FSO_EXP_SCHRAUDOLPH = 0, FSO_EXP_EXACT = 1 };
-enum { FSO_P_MX = 0, FSO_P_NONE = 1 };
+enum { FSO_P_MX = 0, FSO_P_NONE = 1, FSO_P_EFQ = 2 };
 enum { FSO_FOLD_FP32 = 0, FSO_FOLD_EXACT = 1 };
 
 /* references computed on the same quantized operands */
@@ -115,6 +115,20 @@ int fso_quantize_mx_rmsnorm(const uint16_t* src, int64_t n_mat, int64_t rows, in
 /* Schraudolph stage 1: fp32 folded score -> BF16 bit pattern */
 uint16_t fso_stage1(float t);
 
+/*
+ * R24, EFQ-style direct E2M1 P of one 32-key block ("EFQ-Softmax: Exp-Free
+ * Quantization for Softmax", sections II.B-C, III.B): from the block's folded
+ * binary32 scores t[0..nvis) (keys nvis..31 absent: code 0; nvis = 0: E8M0 0),
+ *   E    = floor(fl32(max t - T0) / 128)      (exponent of the block maximum)
+ *   E8M0 = clamp(E - 2 + 127, 0, 254)
+ *   a    = fl32(1 / fl32(128 h)),  base = fl32(fl32(T0 + 128 E) + fl32(128 tau)),
+ *   b    = -fl32(base a),  u_k = fma32(t_k, a, b),
+ *   code = clamp(floor(u_k), 0, 7)           (E2M1 codes 0..7 = 0 .. 6.0)
+ * i.e. code = #{j in 1..7 : r_k >= tau + j h} for the residual
+ * r_k = (t_k - T0) / 128 - E, up to the binary32 rounding of u_k.
+ */
+void fso_efq_block(const float* t, int nvis, float T0, double tau, double h, uint8_t* codes, uint8_t* scale);
+
 typedef struct {
   int B, H, Sq, Skv, D;
   int qk_elem, v_elem, p_elem, scale_rule;
@@ -123,6 +137,10 @@ typedef struct {
   int kv_tile;       /* keys per gate tile, multiple of 32 */
   int exp_mode, p_mode, fold_mode;
   int nthreads;      /* <= 0: all online CPUs */
+  /* p_mode FSO_P_EFQ (R24, needs p_elem E2M1 and the binary32 fold): the
+   * threshold shift tau and spacing h, in log2 units; h in [1/64, 16],
+   * tau in [-64, 64] */
+  double efq_tau, efq_h;
 } fso_params;
 
 /*

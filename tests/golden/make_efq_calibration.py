@@ -1,0 +1,127 @@
+"""Offline calibration of the EFQ-style P rule's (tau, h) on synthetic data.
+
+"EFQ-Softmax: Exp-Free Quantization for Softmax", section III.B: the
+threshold shift tau and spacing h are chosen offline by minimizing the
+attention-output error over representative score blocks, then fixed.  No
+model score blocks are available here, so the representative data are the
+seeded synthetic inputs of the error study (iid N(0,1) Q/K/V) and of the
+qk-normed recipe, with MXFP4 operands (E2M1 Q/K/V), the format the EFQ page
+pairs its P with.  The objective is the relative Frobenius error of the
+output against exact softmax on the same quantized operands (reference R1:
+unquantized P, same V-hat), so that it measures the P rule alone.
+
+Calls only the oracle and the seeded input generators.  Writes
+tests/golden/efq_calibration.json:
+    python tests/golden/make_efq_calibration.py
+"""
+import json
+import math
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from softmax_matrix_cores_amd import workloads as W  # noqa: E402
+
+OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "efq_calibration.json")
+S, D = 1024, 128
+E2M1, E2M3 = oracle.E2M1, oracle.E2M3
+
+
+def bits(x):
+    return x.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+
+
+def datasets():
+    """(name, Q, K, V, sigma, B, H) with MXFP4 operands from the oracle's quantizer."""
+    sets = []
+    sigma = 1 / math.sqrt(D)
+    a = oracle.softmax_scale_prescale(sigma)
+    for seed in range(3):
+        q, k, v = W.error_study_inputs(seed, S=S, D=D)
+        sets.append((f"iid-seed{seed}", q, k, v))
+    w = W.custom("qknorm-mxfp4", B=1, H=2, Sq=S, Skv=S, D=D)
+    q, k, v = W.make_inputs(w)
+    sets.append(("qknorm-H2", q, k, v))
+    out = []
+    for name, q, k, v in sets:
+        B, H = q.shape[0], q.shape[1]
+        n = B * H
+        Q = oracle.quantize_mx(bits(q).reshape(n, S, D), 0, E2M1, prescale=a)
+        K = oracle.quantize_mx(bits(k).reshape(n, S, D), 0, E2M1)
+        V = oracle.quantize_mx(bits(v).reshape(n, S, D), 1, E2M1)
+        p = oracle.make_params(B, H, S, S, D, E2M1, E2M1, E2M3, tau=8.0, kv_tile=64)
+        R1 = oracle.reference(p, oracle.REF_R1, Q, K, V)
+        out.append((name, Q, K, V, B, H, R1))
+    return out
+
+
+def error(data, tau, h):
+    errs = []
+    for name, Q, K, V, B, H, R1 in data:
+        p = oracle.make_params(B, H, S, S, D, E2M1, E2M1, E2M1, tau=8.0, kv_tile=64, p_mode=oracle.P_EFQ,
+                               efq_tau=tau, efq_h=h)
+        O = oracle.forward(p, Q, K, V)["O"]
+        errs.append(np.linalg.norm(O - R1) / np.linalg.norm(R1))
+    return float(np.mean(errs)), errs
+
+
+def main():
+    oracle.build(force=False)
+    data = datasets()
+    best = None
+    grid = []
+    # coarse: h in [1/4, 1] step 1/16, tau in [-6, -1] step 1/8
+    for h in np.arange(4, 17) / 16:
+        for tau in np.arange(-48, -7) / 8:
+            e, _ = error(data, float(tau), float(h))
+            grid.append((float(tau), float(h), e))
+            if best is None or e < best[2]:
+                best = (float(tau), float(h), e)
+    coarse = best
+    # fine: h +-1/16 and tau +-1/8 around the coarse optimum, step 1/64
+    for dh in range(-4, 5):
+        for dt in range(-8, 9):
+            h, tau = coarse[1] + dh / 64, coarse[0] + dt / 64
+            if not (1 / 64 <= h <= 16):
+                continue
+            e, _ = error(data, tau, h)
+            if e < best[2]:
+                best = (tau, h, e)
+    tau, h, e = best
+    _, per = error(data, tau, h)
+    # the fused method's own two-stage P on the same operands, for comparison:
+    # E2M3 (its six-bit P) and E2M1 (the same four-bit output set as the rule)
+    two = {E2M3: [], E2M1: []}
+    for name, Q, K, V, B, H, R1 in data:
+        for pe in two:
+            p = oracle.make_params(B, H, S, S, D, E2M1, E2M1, pe, tau=8.0, kv_tile=64)
+            O = oracle.forward(p, Q, K, V)["O"]
+            two[pe].append(float(np.linalg.norm(O - R1) / np.linalg.norm(R1)))
+    res = {
+        "source": "EFQ-Softmax: Exp-Free Quantization for Softmax, section III.B (offline calibration of tau, h); "
+                  "the data are synthetic stand-ins (no model score blocks)",
+        "script": "tests/golden/make_efq_calibration.py (oracle only)",
+        "data": [d[0] for d in data],
+        "shape": {"S": S, "D": D, "formats": "E2M1 Q/K/V, E2M1 P, gate tau 8, 64-key gate tiles"},
+        "objective": "mean relative Frobenius error of O against R1 (exact softmax on the quantized scores)",
+        "grid": "coarse h 1/4..1 step 1/16, tau -6..-1 step 1/8; fine step 1/64 around the coarse optimum",
+        "efq_tau": tau,
+        "efq_h": h,
+        "error": e,
+        "error_per_set": dict(zip([d[0] for d in data], [float(x) for x in per])),
+        "two_stage_e2m3_error_per_set": dict(zip([d[0] for d in data], two[E2M3])),
+        "two_stage_e2m1_error_per_set": dict(zip([d[0] for d in data], two[E2M1])),
+    }
+    with open(OUT, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    main()
