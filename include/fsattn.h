@@ -153,7 +153,7 @@ typedef struct {
   int Sq, Skv;           /* query and key counts (>= 1 for Skv, any length: tails are masked) */
   int D;                 /* head dimension: 64 or 128 */
   float softmax_scale;   /* sigma; must equal q->prescale / (128 log2 e) to within 2 ulp */
-  int p_elem;            /* element format of P: E4M3 or E2M3 */
+  int p_elem;            /* element format of P: E4M3 or E2M3 (E2M1: fsattn_forward_efq only) */
   float tau;             /* rollback threshold in log2 units of P, >= 0 (default 8) */
   float schraudolph_c;   /* shift c in BF16-pattern units (default 0) */
   int kv_tile;           /* keys per gate tile: 64 or 128 */
@@ -222,6 +222,38 @@ typedef struct {
 
 int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
                           const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream);
+
+/*
+ * fsattn_forward_efq -- the forward with P generated directly as MXFP4
+ * (E2M1 codes, one E8M0 per 32 keys) by an EFQ-style affine rule in the log
+ * domain, in place of stage 1 and stage 2 ("EFQ-Softmax: Exp-Free
+ * Quantization for Softmax", paperlayer.ai summary of arXiv 2609.09721,
+ * sections II.B-C and III.A-B).  Everything else (the fold, the frozen
+ * reference, the rollback gate, masks, O += P V and l += P 1 with the same P)
+ * is fsattn_forward_masked's.  For each 32-key block of P and its folded
+ * binary32 scores t (after the tile's gate shift; masked keys excluded):
+ *   E    = floor(fl32(max t - T0) / 128) clamped to [-1000, 1000]
+ *          (the exponent of the block's largest probability; the reference
+ *          maps to T0)
+ *   E8M0 = clamp(E - 2 + 127, 0, 254)
+ *   a    = fl32(1 / fl32(128 efq_h)),  base = fl32(fl32(T0 + 128 E) + 128 efq_tau),
+ *   b    = -fl32(base a),  code = clamp(floor(fma32(t, a, b)), 0, 7)
+ * i.e. the residual r = (t - T0)/128 - E is compared with the uniformly spaced
+ * thresholds efq_tau + j efq_h (j = 1..7); code 7 is E2M1's 6.0; masked keys
+ * get code 0.  (efq_tau, efq_h) are calibrated offline; -3.890625 and
+ * 0.609375 minimize the output error on synthetic MXFP4 attention.
+ *
+ * p->p_elem must be FSATTN_E2M1; Q/K/V are all E2M3 or all E2M1.  A P dump
+ * (p_dump_codes) holds the E2M1 codes.  efq_h in [1/64, 16], efq_tau in
+ * [-64, 64].  mask may be NULL.
+ * Errors: as fsattn_forward_masked; FSATTN_E_INVALID_ARG also for p_elem not
+ * E2M1 or (efq_tau, efq_h) out of range; FSATTN_E_UNSUPPORTED for other
+ * Q/K/V formats.  (fsattn_forward and fsattn_forward_masked return
+ * FSATTN_E_UNSUPPORTED for p_elem E2M1.)
+ */
+int fsattn_forward_efq(const fsattn_params* p, const fsattn_mask* mask, float efq_tau, float efq_h,
+                       const fsattn_mx_tensor* q, const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out,
+                       void* stream);
 
 /*
  * fsattn_forward_bf16_baseline -- conventional attention forward in BF16

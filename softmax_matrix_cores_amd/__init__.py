@@ -27,8 +27,13 @@ SCALE_FITMAX, SCALE_OCP_FLOOR = 0, 1
 ABI_SYMBOLS = (
     "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
     "fsattn_quantize_mx", "fsattn_quantize_mx_rmsnorm", "fsattn_forward", "fsattn_forward_masked",
-    "fsattn_forward_bf16_baseline", "fsattn_forward_bf16_baseline_masked",
+    "fsattn_forward_bf16_baseline", "fsattn_forward_bf16_baseline_masked", "fsattn_forward_efq",
 )
+
+# (tau, h) of the EFQ-style E2M1 P rule (fsattn_forward_efq), calibrated offline
+# on synthetic MXFP4 attention by minimizing the output error against exact
+# softmax on the same quantized operands
+EFQ_TAU, EFQ_H = -3.890625, 0.609375
 
 
 class FsattnError(RuntimeError):
@@ -87,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.fsattn_forward_masked.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_Mask),
                                             ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
                                             ctypes.POINTER(_MxTensor), V, V]
+        L.fsattn_forward_efq.restype = I
+        L.fsattn_forward_efq.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_Mask), ctypes.c_float,
+                                         ctypes.c_float, ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
+                                         ctypes.POINTER(_MxTensor), V, V]
         L.fsattn_forward_bf16_baseline.restype = I
         L.fsattn_forward_bf16_baseline.argtypes = [V, V, V, I, I, I, I, I, ctypes.c_float, V, V]
         L.fsattn_forward_bf16_baseline_masked.restype = I
@@ -197,11 +206,14 @@ def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qk_elem, v_e
 def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv: int, D: int, softmax_scale: float,
             p_elem, tau: float = 8.0, c: float = 0.0, kv_tile: int = 64, counts: torch.Tensor | None = None,
             out: torch.Tensor | None = None, p_dump: tuple | None = None, stream=None, causal: bool = False,
-            q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None) -> torch.Tensor:
+            q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None, efq_tau: float = EFQ_TAU,
+            efq_h: float = EFQ_H) -> torch.Tensor:
     """Fused-Softmax attention forward.  Returns bf16 [B,H,Sq,D].
     counts: optional int32 [B,H,Sq] written with rollback counts.
     p_dump: optional (b, h, row0, row1, codes uint8 [rows, Skv32], scales uint8 [rows, Skv32/32]).
-    causal / q_lens / kv_lens: masks (fsattn_forward_masked); lens are device int32 [B]."""
+    causal / q_lens / kv_lens: masks (fsattn_forward_masked); lens are device int32 [B].
+    p_elem "e2m1": P straight from the scores by the EFQ-style rule with (efq_tau, efq_h)
+    (fsattn_forward_efq)."""
     dev = Q.codes.device
     if out is None:
         out = torch.empty(B, H, Sq, D, dtype=torch.bfloat16, device=dev)
@@ -212,13 +224,21 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
         p.p_dump_codes, p.p_dump_scales = pc.data_ptr(), ps.data_ptr()
         p.p_b, p.p_h, p.p_row0, p.p_row1 = b, h, r0, r1
     q, k, v = Q._c(), K._c(), V._c()
-    if causal or q_lens is not None or kv_lens is not None:
+    masked = causal or q_lens is not None or kv_lens is not None
+    if masked:
         for t in (q_lens, kv_lens):
             if t is not None and (t.dtype != torch.int32 or t.device != dev or t.shape != (B,) or
                                   not t.is_contiguous()):
                 raise ValueError("q_lens / kv_lens must be contiguous int32 [B] on the operands' device")
         m = _Mask(1 if causal else 0, q_lens.data_ptr() if q_lens is not None else None,
                   kv_lens.data_ptr() if kv_lens is not None else None)
+    if p.p_elem == ELEMS["e2m1"]:
+        st = lib().fsattn_forward_efq(ctypes.byref(p), ctypes.byref(m) if masked else None, ctypes.c_float(efq_tau),
+                                      ctypes.c_float(efq_h), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                      out.data_ptr(), _stream(stream))
+        _check("fsattn_forward_efq", st)
+        return out
+    if masked:
         st = lib().fsattn_forward_masked(ctypes.byref(p), ctypes.byref(m), ctypes.byref(q), ctypes.byref(k),
                                          ctypes.byref(v), out.data_ptr(), _stream(stream))
         _check("fsattn_forward_masked", st)

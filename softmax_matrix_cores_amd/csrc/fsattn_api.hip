@@ -115,9 +115,19 @@ int fsattn_quantize_mx_rmsnorm(const void* src, int64_t n_mat, int64_t rows, int
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
 }
 
-int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
-                          const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream) {
+// the forward of every entry point; efq: E2M1 P by the EFQ-style rule with
+// (efq_tau, efq_h), else E2M1 P is refused (the two-stage path has no FP4 P)
+static int forward_impl(const fsattn_params* p, const fsattn_mask* mask, bool efq, float efq_tau, float efq_h,
+                        const fsattn_mx_tensor* q, const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out,
+                        void* stream) {
   if (!p || !q || !k || !v) return FSATTN_E_INVALID_ARG;
+  if (efq) {
+    if (p->p_elem != FSATTN_E2M1) return FSATTN_E_INVALID_ARG;
+    if (!(efq_h >= 1.0f / 64.0f && efq_h <= 16.0f) || !(efq_tau >= -64.0f && efq_tau <= 64.0f))
+      return FSATTN_E_INVALID_ARG;
+  } else if (p->p_elem == FSATTN_E2M1) {
+    return FSATTN_E_UNSUPPORTED;
+  }
   if (mask) {
     if (mask->causal != 0 && mask->causal != 1) return FSATTN_E_INVALID_ARG;
     if (!aligned(mask->q_lens, 4) || !aligned(mask->kv_lens, 4)) return FSATTN_E_ALIGNMENT;
@@ -172,14 +182,28 @@ int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const
   a.causal = mask ? mask->causal : 0;
   a.q_lens = mask ? mask->q_lens : nullptr;
   a.kv_lens = mask ? mask->kv_lens : nullptr;
+  // EFQ-style P: slope a = fl32(1 / fl32(128 h)) and 128 tau (exact)
+  a.efq_a = efq ? 1.0f / (128.0f * efq_h) : 0.0f;
+  a.efq_t128 = efq ? 128.0f * efq_tau : 0.0f;
   hipError_t e = fsattn::launch_fsattn_fwd(a, p->B, p->D, q->elem, v->elem, p->p_elem,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
 }
 
+int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
+                          const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream) {
+  return forward_impl(p, mask, false, 0.0f, 0.0f, q, k, v, out, stream);
+}
+
 int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsattn_mx_tensor* k,
                    const fsattn_mx_tensor* v, void* out, void* stream) {
-  return fsattn_forward_masked(p, nullptr, q, k, v, out, stream);
+  return forward_impl(p, nullptr, false, 0.0f, 0.0f, q, k, v, out, stream);
+}
+
+int fsattn_forward_efq(const fsattn_params* p, const fsattn_mask* mask, float efq_tau, float efq_h,
+                       const fsattn_mx_tensor* q, const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out,
+                       void* stream) {
+  return forward_impl(p, mask, true, efq_tau, efq_h, q, k, v, out, stream);
 }
 
 int fsattn_forward_bf16_baseline(const void* q, const void* k, const void* v, int B, int H, int Sq, int Skv, int D,

@@ -233,6 +233,8 @@ __device__ Dma dma_scale(bool kside, int wj, int lane, int ko) {
 // widened at each product, so that no copy carries unused registers)
 template <int PE> struct POp { typedef v6i T; };
 template <> struct POp<E4M3> { typedef v8i T; };
+template <> struct POp<E2M1> { typedef v4i T; };
+__device__ __forceinline__ v8i widen(const v4i& p) { return v8i{p[0], p[1], p[2], p[3], 0, 0, 0, 0}; }
 __device__ __forceinline__ v8i widen(const v6i& p) { return v8i{p[0], p[1], p[2], p[3], p[4], p[5], 0, 0}; }
 __device__ __forceinline__ const v8i& widen(const v8i& p) { return p; }
 
@@ -321,6 +323,54 @@ __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, floa
     dsc[0] = s0;
     dsc[1] = s1;
   }
+}
+
+// EFQ-style P ("EFQ-Softmax: Exp-Free Quantization for Softmax", sections
+// II.B-C, III.B): E2M1 codes straight from the folded scores, no exponential
+// and no BF16 stage.  A lane's 32 scores are one block (element e = 16 kg + k):
+//   E    = floor(fl32(max - T0) / 128), clamped to [-1000, 1000]
+//   E8M0 = clamp(E + 125, 0, 254)                (E2M1's top binade is 2^2)
+//   b    = -fl32(fl32(fl32(T0 + 128 E) + 128 tau) a),  a = fl32(1 / (128 h))
+//   code = clamp(floor(fma(t, a, b)), 0, 7)      (thresholds tau + j h on the
+//                                                 residual (t - T0)/128 - E)
+// Masked keys hold -inf: code 0.  FAST: the block max lies in [T0 - 16000,
+// TgEff], so E is in [-125, 127], no clamp acts and every fma result is below
+// (1 - tau) / h + 1 <= 4161 (h >= 1/64, tau >= -64): it fits the 16-bit
+// halves the codes are packed through.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <bool FAST>
+__device__ __forceinline__ void p_efq(const v16f (&S)[2], float m0, float m1, float T0, float ea, float et128,
+                                      v4i& pA, int& pS, uint32_t (&dsc)[2]) {
+  const float tm = __builtin_fmaxf(m0, m1);
+  float ef = __builtin_floorf((tm - T0) * (1.0f / 128.0f));
+  if (!FAST) ef = __builtin_fminf(__builtin_fmaxf(ef, -1000.0f), 1000.0f);
+  const int E = (int)ef;
+  const uint32_t sc = FAST ? (uint32_t)(E + 125) : (uint32_t)min(max(E + 125, 0), 254);
+  const float base = (T0 + (float)(128 * E)) + et128;
+  const float b = -(base * ea);
+  auto code = [&](int e) -> uint32_t {
+    float u = __builtin_fmaf(S[e >> 4][e & 15], ea, b);
+    if (!FAST) u = __builtin_fminf(u, 7.0f);
+    return __float2uint_rz(u);  // floor for u >= 0, 0 below (and for -inf)
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // dword j holds elements 8j .. 8j+7, element 8j+i in bits [4i, 4i+4):
+    // halves (8j+i, 8j+i+4) are packed first, clamped to 7 together, then
+    // interleaved by nibble
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u16x2 h2 = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(code(8 * j + i + 4), code(8 * j + i), 0x05040100u));
+      h2 = __builtin_elementwise_min(h2, (u16x2){7, 7});
+      w[i] = __builtin_bit_cast(uint32_t, h2);
+    }
+    const uint32_t x = w[0] | (w[1] << 4), y = w[2] | (w[3] << 4);
+    pA[j] = (int)(x | (y << 8));
+  }
+  pS = (int)sc;
+  dsc[0] = sc;
+  dsc[1] = sc;
 }
 
 // optional P dump (debug): one code byte per key and the E8M0 per 32 keys
@@ -564,6 +614,15 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   const float T0 = a.T0, Tg = a.Tg;
   // above TgEff the stage-1 clamp could act: exact path (kept in an SGPR)
   const float TgEff = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fminf(Tg, 32639.0f))));
+  // E2M1 P is the EFQ-style rule (p_efq): its slope and 128 tau
+  constexpr bool EFQ = PE == E2M1;
+  const float ea = a.efq_a, et128 = a.efq_t128;
+  // fast-path lower bound of a block max: the BF16 flush bound, or (EFQ) an
+  // E8M0 that needs no clamp (fl32(max - T0) >= -16000, E >= -125)
+  auto low_ok = [&](float mx) -> float {
+    if constexpr (EFQ) return (mx - T0) + 16000.0f;
+    else return mx - PFlush<PE>::t;
+  };
 
   float C = 0.0f;
   v16f Cv;  // C splat: the accumulator's initial value of the score product
@@ -693,7 +752,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     if constexpr (KV128) {
       if ((u & 1) == 0 && u + 1 < ns) tm = __builtin_fmaxf(tm, mnext);
     }
-    return Check{m0, m1, __builtin_fminf(TgEff - tm, lo - PFlush<PE>::t) >= 0.0f};
+    return Check{m0, m1, __builtin_fminf(TgEff - tm, low_ok(lo)) >= 0.0f};
   };
 
   // exact conversion of step u: masking, reference (FIRST: step 0), gate,
@@ -730,20 +789,24 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
         for (int k = 0; k < 16; ++k) Cv[k] = Cv[k] - delta;
       }
     }
-    float mx0 = -INFINITY, mx1 = -INFINITY;
+    if constexpr (EFQ) {
+      p_efq<false>(S, max16(S[0]), max16(S[1]), T0, ea, et128, pA, pS, dsc);
+    } else {
+      float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg)
+      for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float v = S[kg][k];
-        const float f = (v >= 128.0f) ? __builtin_fminf(v, 32639.5f) : -INFINITY;
-        S[kg][k] = f;
-        if (kg == 0) mx0 = __builtin_fmaxf(mx0, f);
-        else mx1 = __builtin_fmaxf(mx1, f);
-      }
-    uint32_t wv[16];
-    pack_b(S, wv);
-    p_from_w<PE, false>(wv, mx0, mx1, lane, pA, pS, dsc);
+        for (int k = 0; k < 16; ++k) {
+          const float v = S[kg][k];
+          const float f = (v >= 128.0f) ? __builtin_fminf(v, 32639.5f) : -INFINITY;
+          S[kg][k] = f;
+          if (kg == 0) mx0 = __builtin_fmaxf(mx0, f);
+          else mx1 = __builtin_fmaxf(mx1, f);
+        }
+      uint32_t wv[16];
+      pack_b(S, wv);
+      p_from_w<PE, false>(wv, mx0, mx1, lane, pA, pS, dsc);
+    }
   };
 
   // gate-only rare step (64-key gate tiles, one P block per lane, no masked
@@ -759,7 +822,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     const float delta = fire ? mrow - T0 : 0.0f;
     // max(fl32(s - delta)) = fl32(max s - delta): the maps are monotonic
     const float m0 = c.m0 - delta, m1 = c.m1 - delta;
-    const bool ok = fire ? __builtin_fmaxf(m0, m1) >= PFlush<PE>::t : c.ok;
+    const bool ok = fire ? low_ok(__builtin_fmaxf(m0, m1)) >= 0.0f : c.ok;
     if (__ballot(!ok) != 0) return false;
     rho = 1.0f;
     if (fire) {
@@ -773,9 +836,13 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) Cv[k] = Cv[k] - delta;
     }
-    uint32_t wv[16];
-    pack_b(S, wv);
-    p_from_w<PE, true>(wv, m0, m1, lane, pA, pS, dsc);
+    if constexpr (EFQ) {
+      p_efq<true>(S, m0, m1, T0, ea, et128, pA, pS, dsc);
+    } else {
+      uint32_t wv[16];
+      pack_b(S, wv);
+      p_from_w<PE, true>(wv, m0, m1, lane, pA, pS, dsc);
+    }
     return true;
   };
 
@@ -835,11 +902,16 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     else pv_of(pA, pS, read_v(u - 1));
     const Check c = check(S, u, mn);
     const bool rare = (u >= ums) | (__ballot(!c.ok) != 0);
-    uint32_t wv[16], dsc[2];
-    pack_b(S, wv);
+    uint32_t dsc[2];
     PT pAf;
     int pSf;
-    p_from_w<PE, true>(wv, c.m0, c.m1, lane, pAf, pSf, dsc);
+    if constexpr (EFQ) {
+      p_efq<true>(S, c.m0, c.m1, T0, ea, et128, pAf, pSf, dsc);
+    } else {
+      uint32_t wv[16];
+      pack_b(S, wv);
+      p_from_w<PE, true>(wv, c.m0, c.m1, lane, pAf, pSf, dsc);
+    }
     // computed here on every step (not sunk into the fast branch)
     asm volatile("" : "+v"(pAf), "+v"(pSf));
 #pragma unroll
@@ -912,10 +984,12 @@ hipError_t launch_d(const FwdArgs& a, int B, int D, hipStream_t s) {
 
 }  // namespace
 
-// supported combinations: FP8 P with FP8 V; FP6 (E2M3) P with FP6 or FP4 V
+// supported combinations: FP8 P with FP8 V; FP6 (E2M3) P with FP6 or FP4 V;
+// EFQ-style FP4 (E2M1) P with FP6 Q/K/V or FP4 Q/K/V
 bool fwd_supported(int qk, int ve, int pe) {
   if (pe == E4M3) return ve == E4M3 && (qk == E4M3 || qk == E2M3 || qk == E2M1);
   if (pe == E2M3) return (ve == E2M3 || ve == E2M1) && (qk == E4M3 || qk == E2M3 || qk == E2M1);
+  if (pe == E2M1) return (qk == E2M3 && ve == E2M3) || (qk == E2M1 && ve == E2M1);
   return false;
 }
 
@@ -931,6 +1005,8 @@ hipError_t launch_fsattn_fwd(const FwdArgs& a, int B, int D, int qk, int ve, int
   FS_CASE(E2M1, E2M1, E2M3)
   FS_CASE(E2M3, E2M1, E2M3)
   FS_CASE(E4M3, E2M1, E2M3)
+  FS_CASE(E2M3, E2M3, E2M1)
+  FS_CASE(E2M1, E2M1, E2M1)
 #undef FS_CASE
   return hipErrorInvalidValue;
 }

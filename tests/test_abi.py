@@ -148,3 +148,37 @@ def test_bf16_masked_validation():
     assert B(16, 16, 16, 1, 1, 8, 8, 96, f, ctypes.byref(fs._Mask(1, None, None)), 16, None) == -1
     assert B(16, 16, 16, 1, 1, 0, 8, 128, f, ctypes.byref(fs._Mask(1, 16, 16)), 16, None) == 0
     assert B(16, 16, 16, 1, 1, 0, 8, 128, f, None, 16, None) == 0
+
+
+def _call_efq(p, q, k, v, tau=-3.890625, h=0.609375, out=16, mask=None):
+    return fs.lib().fsattn_forward_efq(ctypes.byref(p), mask, ctypes.c_float(tau), ctypes.c_float(h),
+                                       ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out, None)
+
+
+def test_forward_efq_validation_rejects_before_launch():
+    k1, v1 = _mx(prescale=1.0), _mx(prescale=1.0)
+    assert _call_efq(_params(p_elem=2), _mx(), k1, v1) == -1            # P must be E2M1
+    for h in (1 / 128, 17.0, float("nan"), float("inf")):
+        assert _call_efq(_params(p_elem=4), _mx(), k1, v1, h=h) == -1, h
+    for tau in (-65.0, 65.0, float("nan")):
+        assert _call_efq(_params(p_elem=4), _mx(), k1, v1, tau=tau) == -1, tau
+    assert _call_efq(_params(p_elem=4, tau=-1.0), _mx(), k1, v1) == -1  # gate tau
+    # Q/K/V must all be E2M3 or all E2M1
+    assert _call_efq(_params(p_elem=4), _mx(elem=2), k1, _mx(elem=4, prescale=1.0)) == -2
+    assert _call_efq(_params(p_elem=4), _mx(elem=0), _mx(elem=0, prescale=1.0), _mx(elem=0, prescale=1.0)) == -2
+    # a valid call with nothing to do returns OK without launching
+    assert _call_efq(_params(p_elem=4, B=0), _mx(), k1, v1) == 0
+    e4 = _mx(elem=4)
+    assert _call_efq(_params(p_elem=4, H=0), e4, _mx(elem=4, prescale=1.0), _mx(elem=4, prescale=1.0)) == 0
+    bad = fs._MxTensor(2, fs.fold_prescale(128 ** -0.5), 8, 16)
+    assert _call_efq(_params(p_elem=4), bad, k1, v1) == -3               # misaligned codes
+    m = fs._Mask(2, None, None)
+    assert _call_efq(_params(p_elem=4), _mx(), k1, v1, mask=ctypes.byref(m)) == -1  # causal not 0/1
+
+
+def test_efq_defaults_are_the_stored_calibration():
+    """The binding's default (tau, h) for E2M1 P is the point the offline
+    calibration (tests/golden/make_efq_calibration.py, oracle only) stored."""
+    import json
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "efq_calibration.json")))
+    assert (fs.EFQ_TAU, fs.EFQ_H) == (gold["efq_tau"], gold["efq_h"])
