@@ -26,6 +26,7 @@ ELEM_NAMES = {"e4m3": E4M3, "e5m2": E5M2, "e2m3": E2M3, "e3m2": E3M2, "e2m1": E2
 SCALE_FITMAX, SCALE_OCP_FLOOR = 0, 1
 EXP_SCHRAUDOLPH, EXP_EXACT = 0, 1
 P_MX, P_NONE, P_EFQ = 0, 1, 2
+GATE_EXACT, GATE_PATTERN = 0, 1
 FOLD_FP32, FOLD_EXACT = 0, 1
 REF_R1, REF_R2, REF_R2P, REF_R3 = 1, 2, 3, 4
 
@@ -47,6 +48,7 @@ class Params(ctypes.Structure):
         ("tau", ctypes.c_double), ("c", ctypes.c_double), ("kv_tile", ctypes.c_int),
         ("exp_mode", ctypes.c_int), ("p_mode", ctypes.c_int), ("fold_mode", ctypes.c_int),
         ("nthreads", ctypes.c_int), ("efq_tau", ctypes.c_double), ("efq_h", ctypes.c_double),
+        ("gate_mode", ctypes.c_int), ("gate_misses", ctypes.c_void_p),
     ]
 
 
@@ -176,9 +178,9 @@ def quantize_mx_rmsnorm(x_bf16: np.ndarray, elem: int, prescale: float = 1.0, we
 
 def make_params(B, H, Sq, Skv, D, qk_elem, v_elem, p_elem, tau=8.0, c=0.0, kv_tile=64, scale_rule=SCALE_FITMAX,
                 exp_mode=EXP_SCHRAUDOLPH, p_mode=P_MX, fold_mode=FOLD_FP32, nthreads=0, efq_tau=0.0,
-                efq_h=0.5) -> Params:
+                efq_h=0.5, gate_mode=GATE_EXACT) -> Params:
     return Params(B, H, Sq, Skv, D, qk_elem, v_elem, p_elem, scale_rule, float(tau), float(c), kv_tile,
-                  exp_mode, p_mode, fold_mode, nthreads, float(efq_tau), float(efq_h))
+                  exp_mode, p_mode, fold_mode, nthreads, float(efq_tau), float(efq_h), gate_mode, None)
 
 
 def efq_block(t, T0: float, tau: float, h: float, nvis: int | None = None):
@@ -197,7 +199,8 @@ def efq_block(t, T0: float, tau: float, h: float, nvis: int | None = None):
 
 def forward(p: Params, q, k, v, rows=None, want_p=False, causal=False, q_lens=None, kv_lens=None):
     """q, k, v: (codes, scales) tuples in the quantizer layout.  Returns dict.
-    causal / q_lens / kv_lens: the mask of fso_forward_masked (lens: [B] ints)."""
+    causal / q_lens / kv_lens: the mask of fso_forward_masked (lens: [B] ints).
+    With p.gate_mode GATE_PATTERN the dict also holds the per-row "misses"."""
     nrows = p.B * p.H * p.Sq if rows is None else len(rows)
     rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     O = np.zeros((nrows, p.D), np.float64)
@@ -207,6 +210,8 @@ def forward(p: Params, q, k, v, rows=None, want_p=False, causal=False, q_lens=No
     pc = np.zeros((nrows, s32), np.uint8) if want_p else None
     ps = np.zeros((nrows, s32 // 32), np.uint8) if want_p else None
     args = [np.ascontiguousarray(a) for a in (q[0], q[1], k[0], k[1], v[0], v[1])]
+    misses = np.zeros(nrows, np.int32)
+    p.gate_misses = _ptr(misses)
     if causal or q_lens is not None or kv_lens is not None:
         ql = None if q_lens is None else np.ascontiguousarray(q_lens, dtype=np.int32)
         kl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
@@ -221,7 +226,8 @@ def forward(p: Params, q, k, v, rows=None, want_p=False, causal=False, q_lens=No
                                _ptr(cnt), _ptr(pc), _ptr(ps))
     if rc != 0:
         raise ValueError(f"fso_forward failed ({rc})")
-    out = {"O": O, "l": L, "counts": cnt}
+    p.gate_misses = None
+    out = {"O": O, "l": L, "counts": cnt, "misses": misses}
     if want_p:
         out["p_codes"] = pc
         out["p_scales"] = ps

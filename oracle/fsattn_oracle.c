@@ -46,6 +46,9 @@
  *   R19 kv tiles in ascending key order, one pass.
  *   R24 EFQ-style P (p_mode FSO_P_EFQ, see efq_block): E2M1 codes straight
  *       from the folded scores, an exponent-only E8M0 per 32-key block.
+ *   R25 gate shortcut (gate_mode FSO_GATE_PATTERN): the tile fires when its
+ *       largest stage-1 BF16 pattern exceeds floor(T_gate); a miss is a tile
+ *       the exact rule (R1, R4) would fire and the shortcut does not.
  *
  *  fl32(x) below means round-to-nearest-even of the exact x to binary32.
  */
@@ -593,6 +596,7 @@ typedef struct {
   double* O;
   double* L;
   int32_t* counts;
+  int32_t* misses; /* R25: per row, tiles the exact rule fires and the shortcut does not */
   uint8_t* pcodes;
   uint8_t* pscales;
   /* per-head decoded K/V, shared read-only */
@@ -664,6 +668,24 @@ static int64_t last_visible_key(int64_t Sq, int64_t Skv, int64_t H, const fso_ma
   return lim < -1 ? -1 : lim;
 }
 
+/* The gate decision of a tile with maximum tmax (tiles j >= 1).  Exact rule
+ * (R1, R4): tmax > T_gate.  Shortcut (R25): the fastest 4-bit kernel of the
+ * pages gates through a shortcut that can miss a recovery trigger in an
+ * extreme-score range ["Fused-Softmax shifts an AI attention bottleneck onto
+ * faster GPU hardware", paragraph 12]; the pages do not describe it.  The
+ * reading here: the decision is taken on the stage-1 BF16 patterns the
+ * two-stage conversion produces anyway, stage1(tmax) > floor(T_gate).  It
+ * misses (a) tiles whose max lies in (T_gate, floor(T_gate) + 1), less than
+ * one pattern step above the threshold, and (b) every tile once
+ * floor(T_gate) >= 0x7F7F, where the clamped pattern cannot exceed it. */
+static int gate_fires(const fso_params* p, double tmax, double Tg, int32_t* miss) {
+  const int exact_fire = tmax > Tg;
+  if (p->gate_mode != FSO_GATE_PATTERN) return exact_fire;
+  const int fire = (double)stage1_d(tmax) > floor(Tg);
+  if (exact_fire && !fire) ++*miss;
+  return fire;
+}
+
 static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
   const fso_params* p = J->p;
   int D = p->D, nbd = D / 32;
@@ -678,13 +700,14 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
   double* O = J->O + ri * D;
   for (int d = 0; d < D; ++d) O[d] = 0.0;
   double l = 0.0;
-  int32_t cnt = 0;
+  int32_t cnt = 0, miss = 0;
   memset(rb->pc, 0, (size_t)S32);
   memset(rb->psc, 0, (size_t)(S32 / 32));
   if (Skv == 0) {
     /* no visible key: O = 0, l = 0 */
     if (J->L) J->L[ri] = 0.0;
     if (J->counts) J->counts[ri] = 0;
+    if (J->misses) J->misses[ri] = 0;
     if (J->pcodes) memset(J->pcodes + ri * S32, 0, (size_t)S32);
     if (J->pscales) memset(J->pscales + ri * (S32 / 32), 0, (size_t)(S32 / 32));
     return;
@@ -729,7 +752,7 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
       /* frozen reference (R2): the row max maps to T0 */
       C = exact ? (T0 - tmax) : (double)(float)(T0 - tmax);
       for (int64_t k = k0; k < k1; ++k) rb->tmp[k] = exact ? rb->tmp[k] + C : (double)(float)(rb->tmp[k] + C);
-    } else if (tmax > Tg) {
+    } else if (gate_fires(p, tmax, Tg, &miss)) {
       /* rollback gate (R1, R3, R4, R5) [FS-news 5]: shift that brings this
        * tile's max back to T0 */
       double delta = exact ? (tmax - T0) : (double)(float)(tmax - T0);
@@ -790,6 +813,7 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
   for (int d = 0; d < D; ++d) O[d] /= l;
   if (J->L) J->L[ri] = l;
   if (J->counts) J->counts[ri] = cnt;
+  if (J->misses) J->misses[ri] = miss;
   if (J->pcodes) memcpy(J->pcodes + ri * S32, rb->pc, (size_t)S32);
   if (J->pscales) memcpy(J->pscales + ri * (S32 / 32), rb->psc, (size_t)(S32 / 32));
   (void)head;
@@ -904,6 +928,7 @@ static int check_params(const fso_params* p) {
   } else if (p->p_mode != FSO_P_MX && p->p_mode != FSO_P_NONE) {
     return 0;
   }
+  if (p->gate_mode != FSO_GATE_EXACT && p->gate_mode != FSO_GATE_PATTERN) return 0;
   return 1;
 }
 
@@ -923,6 +948,7 @@ static int run_rows(const fso_params* p, const fso_mask* mask, int ref, const ui
   memset(&J, 0, sizeof J);
   J.p = p; J.mask = mask; J.ref = ref; J.qc = qc; J.qs = qs; J.kc = kc; J.ks = ks; J.vc = vc; J.vs = vs;
   J.rows = rows; J.nrows = nrows; J.O = out_O; J.L = out_l; J.counts = counts; J.pcodes = pcodes; J.pscales = pscales;
+  J.misses = p->gate_misses;
   J.kmint = (int64_t*)malloc(sizeof(int64_t) * (size_t)(Skv * D));
   J.kbexp = (int*)malloc(sizeof(int) * (size_t)(Skv * (D / 32)));
   J.vval = (double*)malloc(sizeof(double) * (size_t)(S32 * D));

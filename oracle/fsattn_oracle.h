@@ -50,6 +50,8 @@ enum { FSO_SCALE_FITMAX = 0, FSO_SCALE_OCP_FLOOR = 1 };
 enum { FSO_EXP_SCHRAUDOLPH = 0, FSO_EXP_EXACT = 1 };
 enum { FSO_P_MX = 0, FSO_P_NONE = 1, FSO_P_EFQ = 2 };
 enum { FSO_FOLD_FP32 = 0, FSO_FOLD_EXACT = 1 };
+/* rollback gate: the exact rule, or the pattern shortcut of R25 */
+enum { FSO_GATE_EXACT = 0, FSO_GATE_PATTERN = 1 };
 
 /* references computed on the same quantized operands */
 enum {
@@ -141,6 +143,12 @@ typedef struct {
    * threshold shift tau and spacing h, in log2 units; h in [1/64, 16],
    * tau in [-64, 64] */
   double efq_tau, efq_h;
+  /* R25: gate_mode FSO_GATE_PATTERN fires a tile (j >= 1) when
+   * stage1(max t) > floor(T_gate) instead of max t > T_gate.  gate_misses:
+   * optional output [nrows], per row the tiles the exact rule would fire in
+   * the same state and the chosen rule does not (0 for the exact rule). */
+  int gate_mode;
+  int32_t* gate_misses;
 } fso_params;
 
 /*
