@@ -154,7 +154,8 @@ typedef struct {
   int D;                 /* head dimension: 64 or 128 */
   float softmax_scale;   /* sigma; must equal q->prescale / (128 log2 e) to within 2 ulp */
   int p_elem;            /* element format of P: E4M3 or E2M3 (E2M1: fsattn_forward_efq only) */
-  float tau;             /* rollback threshold in log2 units of P, >= 0 (default 8) */
+  float tau;             /* rollback threshold in log2 units of P, >= 0 (default 8); keep it below
+                            128 - c/128: above, accepted scores can pass the stage-1 clamp */
   float schraudolph_c;   /* shift c in BF16-pattern units (default 0) */
   int kv_tile;           /* keys per gate tile: 64 or 128 */
   int32_t* rollback_counts; /* optional device [B][H][Sq]: fires per query row; NULL = not written */
@@ -254,6 +255,29 @@ int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const
 int fsattn_forward_efq(const fsattn_params* p, const fsattn_mask* mask, float efq_tau, float efq_h,
                        const fsattn_mx_tensor* q, const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out,
                        void* stream);
+
+/*
+ * fsattn_pattern_gate_tau -- the gate threshold for the rollback-gate
+ * shortcut.  The pages report that their fastest 4-bit kernel gates through
+ * a shortcut that can miss a recovery trigger in an extreme-score range
+ * ("Fused-Softmax shifts an AI attention bottleneck onto faster GPU
+ * hardware", cybernoise.de, paragraph 12), without describing it.  Read here
+ * as deciding on the stage-1 BF16 patterns: a tile fires when
+ * stage1(max t) > floor(T_gate), with T_gate = fl32(128 (127 + tau) - c).
+ * For floor(T_gate) < 0x7F7F that is exactly the exact rule (max t > T_gate')
+ * at T_gate' = the largest binary32 below floor(T_gate) + 1; at or above
+ * 0x7F7F the clamped pattern never exceeds it and the shortcut never fires.
+ * This call returns in *tau_out the tau' whose T_gate is T_gate' (FLT_MAX,
+ * which never fires, in the second case); fsattn_forward with tau' then runs
+ * the shortcut at no extra cost.  It misses tiles whose max lies less than
+ * one pattern step above T_gate, and every tile once T_gate >= 0x7F7F.
+ * Note that T_gate >= 0x7F7F (tau >= 128 - c/128) lets the exact gate keep
+ * scores past the stage-1 clamp too.
+ * Host-only, no GPU use.  Errors: FSATTN_E_INVALID_ARG (tau_out NULL, tau < 0
+ * or not finite, c not finite), FSATTN_E_UNSUPPORTED (no binary32 tau'
+ * reproduces T_gate'; does not happen for c = 0).
+ */
+int fsattn_pattern_gate_tau(float tau, float schraudolph_c, float* tau_out);
 
 /*
  * fsattn_forward_bf16_baseline -- conventional attention forward in BF16

@@ -28,6 +28,7 @@ ABI_SYMBOLS = (
     "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
     "fsattn_quantize_mx", "fsattn_quantize_mx_rmsnorm", "fsattn_forward", "fsattn_forward_masked",
     "fsattn_forward_bf16_baseline", "fsattn_forward_bf16_baseline_masked", "fsattn_forward_efq",
+    "fsattn_pattern_gate_tau",
 )
 
 # (tau, h) of the EFQ-style E2M1 P rule (fsattn_forward_efq), calibrated offline
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.fsattn_forward_efq.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_Mask), ctypes.c_float,
                                          ctypes.c_float, ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
                                          ctypes.POINTER(_MxTensor), V, V]
+        L.fsattn_pattern_gate_tau.restype = I
+        L.fsattn_pattern_gate_tau.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_float)]
         L.fsattn_forward_bf16_baseline.restype = I
         L.fsattn_forward_bf16_baseline.argtypes = [V, V, V, I, I, I, I, I, ctypes.c_float, V, V]
         L.fsattn_forward_bf16_baseline_masked.restype = I
@@ -207,14 +210,19 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
             p_elem, tau: float = 8.0, c: float = 0.0, kv_tile: int = 64, counts: torch.Tensor | None = None,
             out: torch.Tensor | None = None, p_dump: tuple | None = None, stream=None, causal: bool = False,
             q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None, efq_tau: float = EFQ_TAU,
-            efq_h: float = EFQ_H) -> torch.Tensor:
+            efq_h: float = EFQ_H, gate: str = "exact") -> torch.Tensor:
     """Fused-Softmax attention forward.  Returns bf16 [B,H,Sq,D].
     counts: optional int32 [B,H,Sq] written with rollback counts.
     p_dump: optional (b, h, row0, row1, codes uint8 [rows, Skv32], scales uint8 [rows, Skv32/32]).
     causal / q_lens / kv_lens: masks (fsattn_forward_masked); lens are device int32 [B].
     p_elem "e2m1": P straight from the scores by the EFQ-style rule with (efq_tau, efq_h)
-    (fsattn_forward_efq)."""
+    (fsattn_forward_efq).
+    gate "pattern": the gate shortcut on stage-1 patterns (fsattn_pattern_gate_tau)."""
     dev = Q.codes.device
+    if gate == "pattern":
+        tau = pattern_gate_tau(tau, c)
+    elif gate != "exact":
+        raise ValueError(f"unknown gate {gate!r}")
     if out is None:
         out = torch.empty(B, H, Sq, D, dtype=torch.bfloat16, device=dev)
     p = _Params(B, H, Sq, Skv, D, softmax_scale, _elem(p_elem), tau, c, kv_tile,
@@ -247,6 +255,14 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
                               _stream(stream))
     _check("fsattn_forward", st)
     return out
+
+
+def pattern_gate_tau(tau: float, c: float = 0.0) -> float:
+    """tau' that makes the exact gate the stage-1 pattern shortcut (fsattn_pattern_gate_tau)."""
+    out = ctypes.c_float()
+    _check("fsattn_pattern_gate_tau", lib().fsattn_pattern_gate_tau(ctypes.c_float(tau), ctypes.c_float(c),
+                                                                    ctypes.byref(out)))
+    return out.value
 
 
 def forward_bf16_baseline(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float,

@@ -1,6 +1,7 @@
 // fsattn_api.hip -- the extern "C" boundary declared in include/fsattn.h:
 // argument validation (before any launch), size helpers, status strings and
 // kernel launches on the caller's stream.  No allocation, no global state.
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -198,6 +199,25 @@ int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const
 int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsattn_mx_tensor* k,
                    const fsattn_mx_tensor* v, void* out, void* stream) {
   return forward_impl(p, nullptr, false, 0.0f, 0.0f, q, k, v, out, stream);
+}
+
+int fsattn_pattern_gate_tau(float tau, float schraudolph_c, float* tau_out) {
+  if (!tau_out || !(tau >= 0.0f) || !isfinite(tau) || !isfinite(schraudolph_c)) return FSATTN_E_INVALID_ARG;
+  const double c = (double)schraudolph_c;
+  auto gate = [&](float t) { return (float)(128.0 * (127.0 + (double)t) - c); };
+  const double f = floor((double)gate(tau));
+  if (!(f < 32639.0)) {
+    // the clamped stage-1 pattern never exceeds floor(T_gate): never fires
+    *tau_out = FLT_MAX;
+    return FSATTN_OK;
+  }
+  // exact threshold: the largest binary32 below floor(T_gate) + 1
+  const float X = nextafterf((float)(f + 1.0), -INFINITY);
+  float t = (float)(((double)X + c) / 128.0 - 127.0);
+  for (int i = 0; i < 8 && gate(t) != X; ++i) t = nextafterf(t, gate(t) < X ? INFINITY : -INFINITY);
+  if (gate(t) != X || t < 0.0f) return FSATTN_E_UNSUPPORTED;
+  *tau_out = t;
+  return FSATTN_OK;
 }
 
 int fsattn_forward_efq(const fsattn_params* p, const fsattn_mask* mask, float efq_tau, float efq_h,

@@ -65,9 +65,12 @@ def same_bytes(gpu: fs.MXTensor, ora, axis: int = 0) -> tuple[bool, bool]:
     return np.array_equal(gc, ora[0].ravel()), np.array_equal(gs4, os_)
 
 
-def oracle_params(O, w: W.Workload, tau=None, kv_tile=None, efq=None):
-    """efq = (tau, h): E2M1 P by the EFQ-style rule (p_mode P_EFQ)."""
+def oracle_params(O, w: W.Workload, tau=None, kv_tile=None, efq=None, gate="exact"):
+    """efq = (tau, h): E2M1 P by the EFQ-style rule (p_mode P_EFQ); gate "pattern":
+    the stage-1 pattern gate shortcut (gate_mode GATE_PATTERN)."""
     kw = {} if efq is None else dict(p_mode=O.P_EFQ, efq_tau=efq[0], efq_h=efq[1])
+    if gate == "pattern":
+        kw["gate_mode"] = O.GATE_PATTERN
     return O.make_params(w.B, w.H, w.Sq, w.Skv, w.D, O.ELEM_NAMES[w.qk_elem], O.ELEM_NAMES[w.v_elem],
                          O.ELEM_NAMES[w.p_elem], tau=w.tau if tau is None else tau,
                          kv_tile=w.kv_tile if kv_tile is None else kv_tile, **kw)
@@ -86,7 +89,7 @@ def p_mismatch(gc, gs, oc, os_) -> float:
 
 
 def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=None, kv_tile=None,
-             check_quant=True, causal=False, q_lens=None, kv_lens=None, efq=None):
+             check_quant=True, causal=False, q_lens=None, kv_lens=None, efq=None, gate="exact"):
     """Full comparison on workload w.  rows: oracle row sample (None = all rows).
     causal / q_lens / kv_lens: masks ([B] lists), sent to both sides.
     efq = (tau, h) for E2M1 P (default: the library's calibrated pair).
@@ -97,7 +100,7 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
     log(f"[case] {w.name} B={w.B} H={w.H} Sq={w.Sq} Skv={w.Skv} D={w.D} {w.qk_elem}/{w.v_elem}/{w.p_elem} "
         f"tau={w.tau if tau is None else tau} kv_tile={w.kv_tile if kv_tile is None else kv_tile}"
         + (f" causal={causal} q_lens={q_lens} kv_lens={kv_lens}" if masked else "")
-        + (f" efq={efq}" if efq is not None else ""))
+        + (f" efq={efq}" if efq is not None else "") + (f" gate={gate}" if gate != "exact" else ""))
     q, k, v = (x.cpu() for x in W.make_inputs(w, device="cuda:0"))
     tau_ = w.tau if tau is None else tau
     kvt = w.kv_tile if kv_tile is None else kv_tile
@@ -120,6 +123,8 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
                   kv_lens=None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device=dev))
     if efq is not None:
         mk.update(efq_tau=efq[0], efq_h=efq[1])
+    if gate != "exact":
+        mk["gate"] = gate
     out = fs.forward(Qg, Kg, Vg, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=tau_, kv_tile=kvt,
                      counts=counts, p_dump=pd, **mk)
     torch.cuda.synchronize()
@@ -130,7 +135,7 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
         res["quant_q"] = same_bytes(Qg, Qo)
         res["quant_k"] = same_bytes(Kg, Ko)
         res["quant_v"] = same_bytes(Vg, Vo, axis=1)
-    p = oracle_params(O, w, tau=tau_, kv_tile=kvt, efq=efq)
+    p = oracle_params(O, w, tau=tau_, kv_tile=kvt, efq=efq, gate=gate)
     row_ids = None if rows is None else np.asarray(rows, dtype=np.int64)
     omk = dict(causal=causal, q_lens=q_lens, kv_lens=kv_lens) if masked else {}
     r = O.forward(p, Qo, Ko, Vo, rows=row_ids, **omk)
@@ -142,6 +147,7 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
     res["rel_frob"] = rel_frob(gout.astype(np.float64), r["O"])
     res["count_mismatch_rows"] = int((gcnt != r["counts"]).sum())
     res["total_counts"] = int(r["counts"].sum())
+    res["oracle_misses"] = int(r["misses"].sum())
     res["finite"] = bool(np.isfinite(gout).all())
     if masked:
         # rows the oracle leaves empty (no visible key, or past q_len) must be exactly 0

@@ -182,3 +182,27 @@ def test_efq_defaults_are_the_stored_calibration():
     import json
     gold = json.load(open(os.path.join(ROOT, "tests", "golden", "efq_calibration.json")))
     assert (fs.EFQ_TAU, fs.EFQ_H) == (gold["efq_tau"], gold["efq_h"])
+
+
+@pytest.mark.parametrize("tau,c", [(0.0, 0.0), (1.0, 0.0), (8.0, 0.0), (2.7, 0.0), (127.0, 0.0), (8.0, 5.5),
+                                   (3.25, -20.0)])
+def test_pattern_gate_tau_gives_the_shifted_threshold(tau, c):
+    """T_gate(tau') is the largest binary32 below floor(T_gate(tau)) + 1."""
+    import math
+    import numpy as np
+    t2 = fs.pattern_gate_tau(tau, c)
+    tg = float(np.float32(128.0 * (127.0 + float(np.float32(tau))) - c))
+    tg2 = float(np.float32(128.0 * (127.0 + t2) - c))
+    assert tg2 == float(np.nextafter(np.float32(math.floor(tg) + 1), np.float32(0)))
+    assert tg2 >= tg
+
+
+def test_pattern_gate_tau_extreme_range_and_errors():
+    import numpy as np
+    assert fs.pattern_gate_tau(128.0) == float(np.finfo(np.float32).max)
+    assert fs.pattern_gate_tau(500.0) == float(np.finfo(np.float32).max)
+    out = ctypes.c_float()
+    L = fs.lib()
+    assert L.fsattn_pattern_gate_tau(ctypes.c_float(-1.0), ctypes.c_float(0.0), ctypes.byref(out)) == -1
+    assert L.fsattn_pattern_gate_tau(ctypes.c_float(float("nan")), ctypes.c_float(0.0), ctypes.byref(out)) == -1
+    assert L.fsattn_pattern_gate_tau(ctypes.c_float(1.0), ctypes.c_float(0.0), None) == -1
