@@ -20,6 +20,7 @@ import os
 import sys
 
 import numpy as np
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 sys.path.insert(0, ROOT)
@@ -33,7 +34,7 @@ E2M1, E2M3 = oracle.E2M1, oracle.E2M3
 
 
 def bits(x):
-    return x.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    return x.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
 def datasets():
