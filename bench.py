@@ -294,7 +294,7 @@ def main():
 
     variants = [w]
     if args.also == "auto" and w.name.startswith("video-"):
-        variants += [W.WORKLOADS[n] for n in ("video-mxfp6", "video-mxfp4", "video-efq") if n != w.name]
+        variants += [W.WORKLOADS[n] for n in ("video-mxfp6", "video-mxfp4", "video-mxfp8", "video-efq") if n != w.name]
     elif args.also not in ("auto", "none", ""):
         variants += [W.WORKLOADS[n] for n in args.also.split(",")]
 
