@@ -250,21 +250,27 @@ __device__ __forceinline__ uint32_t p_scale(uint32_t bmax) {
 __device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
 
 // Stage 1 + pack: BF16 patterns of a lane's 32 scores (element e = 16 kg + k);
-// v_cvt_u32_f32 truncates toward zero (= floor for t >= 0) and gives 0 below 0
-__device__ __forceinline__ void pack_b(const v16f (&S)[2], uint32_t (&w)[16]) {
+// v_cvt_u32_f32 truncates toward zero (= floor for t >= 0) and gives 0 below 0.
+// The odd element's convert writes straight into the high half of the word
+// (SDWA dst_sel WORD_1, low half preserved): two instructions per pair.  The
+// patterns fit 16 bits (the callers clamp at 0x7F7F or prove the bound), so
+// the half taken is the whole value.  The compiler does not form SDWA from
+// this pattern, hence the inline assembly; it takes the lane maxima d0 / d1
+// of S[0] / S[1] as an operand so that it issues after the instructions that
+// computed them, which read the same score registers through the compiler and
+// so carry whatever wait states a matrix-core result requires.
+__device__ __forceinline__ void pack_b(const v16f (&S)[2], uint32_t (&w)[16], float d0, float d1) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int kg = i >> 3, k = 2 * (i & 7);
-    w[i] = __builtin_amdgcn_perm(__float2uint_rz(S[kg][k + 1]), __float2uint_rz(S[kg][k]), 0x05040100u);
+    uint32_t x = __float2uint_rz(S[kg][k]);
+    asm("v_cvt_u32_f32_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+        : "+v"(x)
+        : "v"(S[kg][k + 1]), "v"(kg ? d1 : d0));
+    w[i] = x;
   }
 }
 
-// half of pack_b: key group kg (patterns 8 kg .. 8 kg + 7)
-__device__ __forceinline__ void pack_half(const v16f (&S)[2], uint32_t (&w)[16], int kg) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    w[8 * kg + i] = __builtin_amdgcn_perm(__float2uint_rz(S[kg][2 * i + 1]), __float2uint_rz(S[kg][2 * i]), 0x05040100u);
-}
 
 __device__ __forceinline__ float max16(const v16f& s) {
   float m = max3f(s[0], s[1], s[2]);
@@ -804,7 +810,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
           else mx1 = __builtin_fmaxf(mx1, f);
         }
       uint32_t wv[16];
-      pack_b(S, wv);
+      pack_b(S, wv, mx0, mx1);
       p_from_w<PE, false>(wv, mx0, mx1, lane, pA, pS, dsc);
     }
   };
@@ -840,7 +846,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       p_efq<true>(S, m0, m1, T0, ea, et128, pA, pS, dsc);
     } else {
       uint32_t wv[16];
-      pack_b(S, wv);
+      pack_b(S, wv, m0, m1);
       p_from_w<PE, true>(wv, m0, m1, lane, pA, pS, dsc);
     }
     return true;
@@ -909,7 +915,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       p_efq<true>(S, c.m0, c.m1, T0, ea, et128, pAf, pSf, dsc);
     } else {
       uint32_t wv[16];
-      pack_b(S, wv);
+      pack_b(S, wv, c.m0, c.m1);
       p_from_w<PE, true>(wv, c.m0, c.m1, lane, pAf, pSf, dsc);
     }
     // computed here on every step (not sunk into the fast branch)
