@@ -625,6 +625,13 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   const float ea = a.efq_a, et128 = a.efq_t128;
   // fast-path lower bound of a block max: the BF16 flush bound, or (EFQ) an
   // E8M0 that needs no clamp (fl32(max - T0) >= -16000, E >= -125)
+  // the fast-path range PFlush <= max <= TgEff as one unsigned compare of the
+  // float bits: both bounds are positive, so a smaller, negative, infinite or
+  // NaN max lands outside [0, RG1) after the subtraction (RG1 = 0: empty)
+  const uint32_t RG1 = __builtin_amdgcn_readfirstlane(
+      TgEff >= PFlush<EFQ ? E2M3 : PE>::t
+          ? __float_as_uint(TgEff) - __float_as_uint(PFlush<EFQ ? E2M3 : PE>::t) + 1u
+          : 0u);
   auto low_ok = [&](float mx) -> float {
     if constexpr (EFQ) return (mx - T0) + 16000.0f;
     else return mx - PFlush<PE>::t;
@@ -758,7 +765,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     if constexpr (KV128) {
       if ((u & 1) == 0 && u + 1 < ns) tm = __builtin_fmaxf(tm, mnext);
     }
-    return Check{m0, m1, __builtin_fminf(TgEff - tm, low_ok(lo)) >= 0.0f};
+    if constexpr (!Opd<PE>::split && !KV128 && !EFQ)
+      return Check{m0, m1, __float_as_uint(tm) - __float_as_uint(PFlush<PE>::t) < RG1};
+    else
+      return Check{m0, m1, __builtin_fminf(TgEff - tm, low_ok(lo)) >= 0.0f};
   };
 
   // exact conversion of step u: masking, reference (FIRST: step 0), gate,
@@ -767,7 +777,13 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   bool any_fire = false;
   auto exact = [&](v16f (&S)[2], int u, float mnext, uint32_t (&dsc)[2], auto first_t) {
     constexpr bool FIRST = decltype(first_t)::value;
-    if (u >= ums) mask(S, lim - u * KS);
+    if (u >= ums) {
+      // the limit is formed here, on the rare path (kept from becoming a
+      // per-lane counter stepped on every step)
+      int uks = u * KS;
+      asm volatile("" : "+s"(uks));
+      mask(S, lim - uks);
+    }
     float m = max32(S);
     if constexpr (KV128) {
       if ((u & 1) == 0 && u + 1 < ns) m = __builtin_fmaxf(m, mnext);
