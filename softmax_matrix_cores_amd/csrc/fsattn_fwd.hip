@@ -39,7 +39,8 @@
 //   * scales: one dword per key holds its K block scales; V scales come in the
 //     quantizer's interleaved layout, one dword per lane holding the scales of
 //     its PV instructions, picked with op_sel.
-//   * fast path per score: one float->int convert (stage 1), half a pack and
+//   * fast path per score: one float->int convert (stage 1; the odd score of
+//     a pair converts straight into the high half of the packed word) and
 //     half a max3.  The E8M0 of P comes from the block max with integer
 //     exponent arithmetic; one v_cvt_scalef32_pk32_fp6_bf16 converts a lane's
 //     32 keys.  A wave ballot sends a step to the exact path on the first
