@@ -940,10 +940,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int o = 0; o < NV; ++o) pin16(O[o]);
     asm volatile("" : "+v"(L));
-    // one PV product per group of VALU work (VALU per product: 11 with FP6
-    // operands, 15 otherwise, as measured; with 11 the P conversion lands
-    // after the last product, so the new P needs almost no copies)
-    constexpr int VPG = (Opd<QK>::tail == 8) ? 11 : 15;
+    // one PV product per group of VALU work, as measured: 40 with FP8 P (its
+    // pair converters make the conversion long), 11 with FP6 operands (the
+    // P conversion then lands after the last product, so the new P needs
+    // almost no copies), 15 otherwise
+    constexpr int VPG = Opd<PE>::split ? 40 : ((Opd<QK>::tail == 8) ? 11 : 15);
     __builtin_amdgcn_sched_group_barrier(0x100, 4 * G::DH + 2, 0);
 #pragma unroll
     for (int i = 0; i < NV + 1; ++i) {
