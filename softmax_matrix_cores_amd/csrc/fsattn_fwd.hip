@@ -96,9 +96,10 @@ template <int QK, int VE, int D> struct Geo {
   static constexpr int QRB = D * Fmt<QK>::bits / 8;
   static constexpr int VBB = 4 * Fmt<VE>::bits;
   static constexpr int KSB = D / 32;
-  static constexpr int K_OFF = 0;
-  static constexpr int KS_OFF = NK * Opd<QK>::region;
-  static constexpr int V_OFF = KS_OFF + 256;
+  // K scales first: their reads then carry no constant offset of their own
+  static constexpr int KS_OFF = 0;
+  static constexpr int K_OFF = 256;
+  static constexpr int V_OFF = K_OFF + NK * Opd<QK>::region;
   static constexpr int VS_OFF = V_OFF + NV * Opd<VE>::region;
   static constexpr int SINK_OFF = VS_OFF + 256;  // 1 KiB per slot for padding loads
   static constexpr int SLOT = SINK_OFF + 1024;
@@ -293,8 +294,12 @@ __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, floa
     uint32_t sc;
     if constexpr (FAST) {
       // the block max lies in [PFlush, TgEff]: no flush, clamp or zero code
+      // ((floor(tm) + 127 - thr7) >> 7) - emax as one fma and a convert: for
+      // tm in [PFlush, 32640) tm / 128, the constant and their sum are exact
+      // in binary32, and floor((floor(t) + k) / 128) = floor((t + k) / 128)
       constexpr int thr7 = (int)(Fmt<PE>::mthr23 >> 16);
-      sc = ((__float2uint_rz(tm) + (uint32_t)(127 - thr7)) >> 7) - Fmt<PE>::emax;
+      constexpr float off = (float)(127 - thr7) / 128.0f - (float)Fmt<PE>::emax;
+      sc = __float2uint_rz(__builtin_fmaf(tm, 1.0f / 128.0f, off));
     } else {
       const uint32_t bmax = (tm >= 128.0f) ? min(__float2uint_rz(tm), 0x7F7Fu) : 0u;
       sc = p_scale<PE>(bmax);
@@ -746,11 +751,19 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   int pS = 127;
 
   // fast-path test of step u: the lane's maxima over its two key groups, and
-  // whether every block max is >= PFlush and the gate-tile max <= TgEff
+  // whether the step must leave the fast path (a block max below PFlush or
+  // the gate-tile max above TgEff)
   // (mnext: the maximum of step u + 1 when u starts a 128-key gate tile)
   struct Check {
     float m0, m1;
-    bool ok;
+    bool bad;  // the step cannot take the fast path (as seen by this lane)
+  };
+  // the fast-path test on a lane's block max (one P block per lane, 64-key
+  // gate tiles); the gate-only path evaluates it again rather than carrying
+  // both polarities of the test through the fast path
+  auto ok_of = [&](float tm) -> bool {
+    if constexpr (!EFQ) return __float_as_uint(tm) - __float_as_uint(PFlush<EFQ ? E2M3 : PE>::t) < RG1;
+    else return __builtin_fminf(TgEff - tm, low_ok(tm)) >= 0.0f;
   };
   auto check = [&](const v16f (&S)[2], int u, float mnext) -> Check {
     const float m0 = max16(S[0]), m1 = max16(S[1]);
@@ -767,9 +780,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       if ((u & 1) == 0 && u + 1 < ns) tm = __builtin_fmaxf(tm, mnext);
     }
     if constexpr (!Opd<PE>::split && !KV128 && !EFQ)
-      return Check{m0, m1, __float_as_uint(tm) - __float_as_uint(PFlush<PE>::t) < RG1};
+      return Check{m0, m1, !(__float_as_uint(tm) - __float_as_uint(PFlush<PE>::t) < RG1)};
     else
-      return Check{m0, m1, __builtin_fminf(TgEff - tm, low_ok(lo)) >= 0.0f};
+      return Check{m0, m1, !(__builtin_fminf(TgEff - tm, low_ok(lo)) >= 0.0f)};
   };
 
   // exact conversion of step u: masking, reference (FIRST: step 0), gate,
@@ -845,7 +858,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     const float delta = fire ? mrow - T0 : 0.0f;
     // max(fl32(s - delta)) = fl32(max s - delta): the maps are monotonic
     const float m0 = c.m0 - delta, m1 = c.m1 - delta;
-    const bool ok = fire ? low_ok(__builtin_fmaxf(m0, m1)) >= 0.0f : c.ok;
+    const bool ok = fire ? low_ok(__builtin_fmaxf(m0, m1)) >= 0.0f : ok_of(tm);
     if (__ballot(!ok) != 0) return false;
     rho = 1.0f;
     if (fire) {
@@ -924,7 +937,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     if constexpr (PRE_V) pv_of(pA, pS, vop);
     else pv_of(pA, pS, read_v(u - 1));
     const Check c = check(S, u, mn);
-    const bool rare = (u >= ums) | (__ballot(!c.ok) != 0);
+    const bool rare = (u >= ums) | (__ballot(c.bad) != 0);
     uint32_t dsc[2];
     PT pAf;
     int pSf;
