@@ -249,7 +249,13 @@ __device__ __forceinline__ uint32_t p_scale(uint32_t bmax) {
   return (uint32_t)min(max(e - Fmt<PELEM>::emax, 0), 254);
 }
 
-__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
+// Maxima of scores use IEEE 754-2019 maximum (v_maximum3_f32 on gfx950): unlike
+// fmaxf it needs no quieting of its inputs in IEEE mode, which cost two extra
+// instructions per 16 scores.  On the scores (finite or -inf, never NaN) it
+// differs from fmaxf at most in the sign of a zero maximum, which no decision
+// here depends on (a zero maximum fails the fast-path range either way).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
 // Stage 1 + pack: BF16 patterns of a lane's 32 scores (element e = 16 kg + k);
 // v_cvt_u32_f32 truncates toward zero (= floor for t >= 0) and gives 0 below 0.
@@ -275,12 +281,12 @@ __device__ __forceinline__ void pack_b(const v16f (&S)[2], uint32_t (&w)[16], fl
 
 
 __device__ __forceinline__ float max16(const v16f& s) {
-  float m = max3f(s[0], s[1], s[2]);
+  float m = vmax3(s[0], s[1], s[2]);
 #pragma unroll
-  for (int k = 3; k < 15; k += 2) m = max3f(m, s[k], s[k + 1]);
-  return __builtin_fmaxf(m, s[15]);
+  for (int k = 3; k < 15; k += 2) m = vmax3(m, s[k], s[k + 1]);
+  return vmax(m, s[15]);
 }
-__device__ __forceinline__ float max32(const v16f (&S)[2]) { return __builtin_fmaxf(max16(S[0]), max16(S[1])); }
+__device__ __forceinline__ float max32(const v16f (&S)[2]) { return vmax(max16(S[0]), max16(S[1])); }
 
 // P operand from packed patterns and the lane's maxima over key groups 0/1.
 // FP6 P: the lane's 32 keys are one block.  FP8 P: elements 0-15 belong to
