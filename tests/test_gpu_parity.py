@@ -41,6 +41,24 @@ def test_small_cases(oracle, name, base, kw, kv_tile):
     assert_ok(res)
 
 
+# every Q/K, V, P format combination the library accepts (EFQ-style E2M1 P
+# has its own tests), alternating the head dimension
+COMBOS = [("e4m3", "e4m3", "e4m3"), ("e2m3", "e4m3", "e4m3"), ("e2m1", "e4m3", "e4m3"),
+          ("e2m3", "e2m3", "e2m3"), ("e2m1", "e2m3", "e2m3"), ("e4m3", "e2m3", "e2m3"),
+          ("e2m1", "e2m1", "e2m3"), ("e2m3", "e2m1", "e2m3"), ("e4m3", "e2m1", "e2m3")]
+
+
+@pytest.mark.parametrize("i", range(len(COMBOS)), ids=["-".join(c) for c in COMBOS])
+def test_every_format_combination(oracle, i):
+    qk, ve, pe = COMBOS[i]
+    w = W.custom("stress-mxfp8", name=f"combo-{qk}-{ve}-{pe}", B=1, H=2, Sq=100, Skv=333, D=(64, 128)[i % 2],
+                 seed=40 + i, qk_elem=qk, v_elem=ve, p_elem=pe)
+    res = run_case(oracle, w, dump_head=(0, 1), dump_rows=(0, 40))
+    assert_ok(res, defer_p=True)
+    assert res["total_counts"] > 0, res  # the stress keys fire the gate
+    check_p(res)
+
+
 @pytest.mark.parametrize("tau", [0.0, 2.0, 1e4])
 @pytest.mark.parametrize("elems", [("e2m3", "e2m3", "e2m3"), ("e4m3", "e4m3", "e4m3"), ("e2m1", "e2m1", "e2m3")])
 def test_tau_sweep(oracle, tau, elems):
