@@ -366,20 +366,26 @@ __device__ __forceinline__ void p_efq(const v16f (&S)[2], float m0, float m1, fl
   const uint32_t sc = FAST ? (uint32_t)(E + 125) : (uint32_t)min(max(E + 125, 0), 254);
   const float base = (T0 + (float)(128 * E)) + et128;
   const float b = -(base * ea);
-  auto code = [&](int e) -> uint32_t {
+  auto ucode = [&](int e) -> float {
     float u = __builtin_fmaf(S[e >> 4][e & 15], ea, b);
     if (!FAST) u = __builtin_fminf(u, 7.0f);
-    return __float2uint_rz(u);  // floor for u >= 0, 0 below (and for -inf)
+    return u;
   };
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     // dword j holds elements 8j .. 8j+7, element 8j+i in bits [4i, 4i+4):
     // halves (8j+i, 8j+i+4) are packed first, clamped to 7 together, then
-    // interleaved by nibble
+    // interleaved by nibble.  The float -> u32 converts truncate (floor for
+    // u >= 0, 0 below and for -inf); the high half's convert writes straight
+    // into the upper 16 bits (SDWA), its input being an fma result
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      u16x2 h2 = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(code(8 * j + i + 4), code(8 * j + i), 0x05040100u));
+      uint32_t xw = __float2uint_rz(ucode(8 * j + i));
+      asm("v_cvt_u32_f32_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+          : "+v"(xw)
+          : "v"(ucode(8 * j + i + 4)));
+      u16x2 h2 = __builtin_bit_cast(u16x2, xw);
       h2 = __builtin_elementwise_min(h2, (u16x2){7, 7});
       w[i] = __builtin_bit_cast(uint32_t, h2);
     }
@@ -960,10 +966,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     for (int o = 0; o < NV; ++o) pin16(O[o]);
     asm volatile("" : "+v"(L));
     // one PV product per group of VALU work, as measured: 40 with FP8 P (its
-    // pair converters make the conversion long), 11 with FP6 operands (the
-    // P conversion then lands after the last product, so the new P needs
-    // almost no copies), 15 otherwise
-    constexpr int VPG = Opd<PE>::split ? 40 : ((Opd<QK>::tail == 8) ? 11 : 15);
+    // pair converters make the conversion long), 11 with FP6 operands or
+    // EFQ-style P (with FP6 operands the P conversion then lands after the
+    // last product, so the new P needs almost no copies), 15 otherwise
+    constexpr int VPG = Opd<PE>::split ? 40 : ((EFQ || Opd<QK>::tail == 8) ? 11 : 15);
     __builtin_amdgcn_sched_group_barrier(0x100, 4 * G::DH + 2, 0);
 #pragma unroll
     for (int i = 0; i < NV + 1; ++i) {
