@@ -307,6 +307,25 @@ int fsattn_forward_bf16_baseline_masked(const void* q, const void* k, const void
                                         int D, float softmax_scale, const fsattn_mask* mask, void* out,
                                         void* stream);
 
+/*
+ * fsattn_probe_mfma -- measurement helper, not part of the attention path.
+ * Runs a kernel that only issues matrix products: `workgroups` workgroups of
+ * eight waves (two per SIMD, as the fused forward), each wave `iters` rounds
+ * of four independent accumulator chains of one 32x32x64 product per round
+ * (fmt FSATTN_E4M3 / E2M3 / E2M1: the scaled MX product with both operands
+ * in that format) or four 32x32x16 BF16 products (FSATTN_PROBE_BF16).
+ * Per wave, flops = iters * 4 * 2*32*32*64.  Wave 0 of workgroup g writes
+ * stamps[4g .. 4g+3] = shader-clock counter (s_memtime) at start and end,
+ * constant-rate counter (s_memrealtime, the device's wall-clock rate) at
+ * start and end, so the caller can derive the matrix-core rate and the
+ * shader clock under that load.  stamps: caller-owned device
+ * uint64 [workgroups][4], 8-byte aligned.
+ * Errors: FSATTN_E_INVALID_ARG (fmt, iters outside [1, 2^32], workgroups
+ * outside [1, 2^20], stamps NULL), FSATTN_E_ALIGNMENT, FSATTN_E_HIP.
+ */
+#define FSATTN_PROBE_BF16 16
+int fsattn_probe_mfma(int fmt, int64_t iters, int workgroups, unsigned long long* stamps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

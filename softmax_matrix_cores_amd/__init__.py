@@ -28,7 +28,7 @@ ABI_SYMBOLS = (
     "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
     "fsattn_quantize_mx", "fsattn_quantize_mx_rmsnorm", "fsattn_forward", "fsattn_forward_masked",
     "fsattn_forward_bf16_baseline", "fsattn_forward_bf16_baseline_masked", "fsattn_forward_efq",
-    "fsattn_pattern_gate_tau",
+    "fsattn_pattern_gate_tau", "fsattn_probe_mfma",
 )
 
 # (tau, h) of the EFQ-style E2M1 P rule (fsattn_forward_efq), calibrated offline
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(_MxTensor), V, V]
         L.fsattn_pattern_gate_tau.restype = I
         L.fsattn_pattern_gate_tau.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_float)]
+        L.fsattn_probe_mfma.restype = I
+        L.fsattn_probe_mfma.argtypes = [I, I64, I, V, V]
         L.fsattn_forward_bf16_baseline.restype = I
         L.fsattn_forward_bf16_baseline.argtypes = [V, V, V, I, I, I, I, I, ctypes.c_float, V, V]
         L.fsattn_forward_bf16_baseline_masked.restype = I
@@ -290,3 +292,17 @@ def forward_bf16_baseline(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sof
                                             ctypes.c_float(softmax_scale), out.data_ptr(), _stream(stream))
     _check("fsattn_forward_bf16_baseline", st)
     return out
+
+
+PROBE_BF16 = 16
+
+
+def probe_mfma(fmt, iters: int, workgroups: int, stream=None) -> torch.Tensor:
+    """Run the pure matrix-product kernel (fsattn_probe_mfma); returns the device
+    int64 stamps [workgroups, 4] (shader clock start/end, wall clock start/end).
+    fmt: an MX element name / code, or "bf16"."""
+    f = PROBE_BF16 if fmt == "bf16" else _elem(fmt)
+    stamps = torch.zeros(workgroups, 4, dtype=torch.int64, device="cuda")
+    _check("fsattn_probe_mfma", lib().fsattn_probe_mfma(f, int(iters), int(workgroups), stamps.data_ptr(),
+                                                        _stream(stream)))
+    return stamps

@@ -251,4 +251,14 @@ int fsattn_forward_bf16_baseline_masked(const void* q, const void* k, const void
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
 }
 
+int fsattn_probe_mfma(int fmt, int64_t iters, int workgroups, unsigned long long* stamps, void* stream) {
+  if (fmt != FSATTN_E4M3 && fmt != FSATTN_E2M3 && fmt != FSATTN_E2M1 && fmt != FSATTN_PROBE_BF16)
+    return FSATTN_E_INVALID_ARG;
+  if (iters < 1 || iters > ((int64_t)1 << 32) || workgroups < 1 || workgroups > (1 << 20) || !stamps)
+    return FSATTN_E_INVALID_ARG;
+  if (!aligned(stamps, 8)) return FSATTN_E_ALIGNMENT;
+  hipError_t e = fsattn::launch_mfma_probe(fmt, iters, workgroups, stamps, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
+}
+
 }  // extern "C"

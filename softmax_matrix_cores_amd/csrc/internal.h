@@ -37,6 +37,7 @@ hipError_t launch_quantize_mx_rmsnorm(const uint16_t* src, int64_t nrows, int64_
                                       uint8_t* codes, uint8_t* scales, hipStream_t stream);
 bool fwd_supported(int qk, int ve, int pe);
 hipError_t launch_fsattn_fwd(const FwdArgs& a, int B, int D, int qk, int ve, int pe, hipStream_t s);
+hipError_t launch_mfma_probe(int elem, int64_t iters, int wgs, unsigned long long* stamps, hipStream_t stream);
 hipError_t launch_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int B, int H,
                            int Sq, int Skv, int D, float softmax_scale, int causal, const int32_t* q_lens,
                            const int32_t* kv_lens, hipStream_t stream);

@@ -133,13 +133,10 @@ def bf16_bits_to_fraction(u16: np.ndarray) -> list[Fraction]:
     return [Fraction(float(v)) for v in f32.ravel()]
 
 
-def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, tau: float = 8.0,
-            kv_tile: int = 64, c: float = 0.0, visible=None):
-    """Tiny forward for one head.  qb [Sq,D], kb/vb [Skv,D] uint16 bf16 bit patterns.
-    visible: optional [Sq] number of keys row i sees (keys 0 .. visible[i]-1);
-    the others are absent (no part in any maximum, P = 0); a row that sees no
-    key gives O = 0.
-    Returns (O [Sq,D] float, counts [Sq], P codes [Sq,Skv32], P scales [Sq,Skv32/32])."""
+def operands(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int):
+    """Exact values of the quantized operands of one head: Q' = fl32(alpha q)
+    quantized along D, K along D, V along keys (zero padded to a multiple of
+    32 keys).  Returns (Qh [Sq][D], Kh [Skv][D], Vh [S32][D]) as Fractions."""
     Sq, D = qb.shape
     Skv = kb.shape[0]
     S32 = (Skv + 31) // 32 * 32
@@ -147,7 +144,7 @@ def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, ta
     Q = [bf16_bits_to_fraction(qb[i]) for i in range(Sq)]
     K = [bf16_bits_to_fraction(kb[i]) for i in range(Skv)]
     V = [bf16_bits_to_fraction(vb[i]) for i in range(Skv)]
-    # operands: Q' = fl32(alpha q) quantized along D; K along D; V along keys (zero padded)
+
     def quant_rows(rows):
         out = []
         for r in rows:
@@ -168,6 +165,55 @@ def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, ta
             X = Fraction(2) ** (sc - 127)
             for j in range(32):
                 Vh[g * 32 + j][d] = value(v_elem, codes[j]) * X
+    return Qh, Kh, Vh
+
+
+def references(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int):
+    """Conventional softmax on the same quantized operands, one head, every
+    query row ("conventional softmax on the same quantized operands" of the
+    pages' error claim).  The exact scores s = sum_d Qh Kh / 128 are in log2
+    units (Q carries 128 log2(e) sigma); p = 2^(s - max s) is evaluated in
+    binary64 from the exactly rounded exponent.  Returns three [Sq][D] arrays:
+      R1   sum p V / sum p                   (P unquantized)
+      R2   sum MX(p) V / sum p               (numerator with P quantized like the
+                                              method's P: 32 consecutive keys per
+                                              block, fit-max E8M0, keys past Skv 0)
+      R2'  sum MX(p) V / sum MX(p)
+    with numerators and denominators accumulated exactly."""
+    Sq, D = qb.shape
+    Skv = kb.shape[0]
+    S32 = (Skv + 31) // 32 * 32
+    Qh, Kh, Vh = operands(qb, kb, vb, sigma, qk_elem, v_elem)
+    out = {name: np.zeros((Sq, D)) for name in ("R1", "R2", "R2'")}
+    for i in range(Sq):
+        s = [sum(a * b for a, b in zip(Qh[i], Kh[k])) / 128 for k in range(Skv)]
+        m = max(s)
+        p = [Fraction(2.0 ** float(x - m)) for x in s] + [Fraction(0)] * (S32 - Skv)
+        ph = []
+        for g in range(S32 // 32):
+            codes, sc = mx_block(p_elem, p[g * 32:(g + 1) * 32])
+            X = Fraction(2) ** (sc - 127)
+            ph += [value(p_elem, cc) * X for cc in codes]
+        num_p = [sum(p[k] * Vh[k][d] for k in range(S32)) for d in range(D)]
+        num_q = [sum(ph[k] * Vh[k][d] for k in range(S32)) for d in range(D)]
+        den_p, den_q = sum(p), sum(ph)
+        out["R1"][i] = [float(x / den_p) for x in num_p]
+        out["R2"][i] = [float(x / den_p) for x in num_q]
+        out["R2'"][i] = [float(x / den_q) for x in num_q]
+    return out
+
+
+def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, tau: float = 8.0,
+            kv_tile: int = 64, c: float = 0.0, visible=None):
+    """Tiny forward for one head.  qb [Sq,D], kb/vb [Skv,D] uint16 bf16 bit patterns.
+    visible: optional [Sq] number of keys row i sees (keys 0 .. visible[i]-1);
+    the others are absent (no part in any maximum, P = 0); a row that sees no
+    key gives O = 0.
+    Returns (O [Sq,D] float, counts [Sq], P codes [Sq,Skv32], P scales [Sq,Skv32/32])."""
+    Sq, D = qb.shape
+    Skv = kb.shape[0]
+    S32 = (Skv + 31) // 32 * 32
+    Qh, Kh, Vh = operands(qb, kb, vb, sigma, qk_elem, v_elem)
     T0 = fl32(Fraction(128 * 127) - Fraction(c))
     Tg = fl32(Fraction(128) * (127 + Fraction(tau)) - Fraction(c))
     O = np.zeros((Sq, D))
