@@ -232,16 +232,19 @@ int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const
  * sections II.B-C and III.A-B).  Everything else (the fold, the frozen
  * reference, the rollback gate, masks, O += P V and l += P 1 with the same P)
  * is fsattn_forward_masked's.  For each 32-key block of P and its folded
- * binary32 scores t (after the tile's gate shift; masked keys excluded):
- *   E    = floor(fl32(max t - T0) / 128) clamped to [-1000, 1000]
- *          (the exponent of the block's largest probability; the reference
- *          maps to T0)
+ * binary32 scores t (after the tile's gate shift; masked keys excluded), with
+ * l = (t - T0) / 128 the score in log2 units (the reference maps to T0):
+ *   E    = floor(max l) clamped to [-1000, 1000] (the exponent of the block's
+ *          largest probability)
  *   E8M0 = clamp(E - 2 + 127, 0, 254)
- *   a    = fl32(1 / fl32(128 efq_h)),  base = fl32(fl32(T0 + 128 E) + 128 efq_tau),
- *   b    = -fl32(base a),  code = clamp(floor(fma32(t, a, b)), 0, 7)
- * i.e. the residual r = (t - T0)/128 - E is compared with the uniformly spaced
- * thresholds efq_tau + j efq_h (j = 1..7); code 7 is E2M1's 6.0; masked keys
- * get code 0.  (efq_tau, efq_h) are calibrated offline; -3.890625 and
+ *   code = #{ j in 1..7 : l - E >= efq_tau + j efq_h }   (code 7 is E2M1's 6.0)
+ * i.e. the residual l - E is compared with uniformly spaced thresholds.  The
+ * kernel evaluates the comparison as clamp(floor(fma32(t, a, b)), 0, 7) with
+ * a = fl32(1 / fl32(128 efq_h)) and b = -fl32(fl32(fl32(T0 + 128 E) +
+ * 128 efq_tau) a); where 1 / (128 efq_h) is not a binary32 value this can
+ * differ from the exact count for scores within about 2^-16 of a threshold
+ * (a P-code difference, inside the method's P-code tolerance).  Masked keys
+ * get code 0.  (efq_tau, efq_h) are calibrated offline; -3.875 and
  * 0.609375 minimize the output error on synthetic MXFP4 attention.
  *
  * p->p_elem must be FSATTN_E2M1; Q/K/V are all E2M3 or all E2M1.  A P dump

@@ -45,7 +45,8 @@
  *   R16 output in fp64 here (the GPU writes bf16).
  *   R19 kv tiles in ascending key order, one pass.
  *   R24 EFQ-style P (p_mode FSO_P_EFQ, see efq_block): E2M1 codes straight
- *       from the folded scores, an exponent-only E8M0 per 32-key block.
+ *       from the folded scores, an exponent-only E8M0 per 32-key block; the
+ *       thresholds are compared in exact arithmetic.
  *   R25 gate shortcut (gate_mode FSO_GATE_PATTERN): the tile fires when its
  *       largest stage-1 BF16 pattern exceeds floor(T_gate); a miss is a tile
  *       the exact rule (R1, R4) would fire and the shortcut does not.
@@ -546,40 +547,38 @@ uint16_t fso_stage1(float t) {
  *  - the shifted score of key k in log2 units is l_k = (t_k - T0) / 128 (the
  *    fold maps the reference to T0);
  *  - exponent-only block scale from the local maximum: E = floor(l_max),
- *    E8M0 = E - 2 + 127 clamped to [0, 254] (E2M1's top binade is 2^2);
+ *    clamped to [-1000, 1000]; E8M0 = E - 2 + 127 clamped to [0, 254]
+ *    (E2M1's top binade is 2^2);
  *  - residual r_k = l_k - E, and codes from uniformly spaced thresholds
- *    tau + j h (j = 1..7): code = clamp(floor((r_k - tau) / h), 0, 7), code 7
- *    being E2M1's 6.0.
- * The integer decisions are taken in binary32, as one fused multiply-add per
- * key: E = floor(fl32(t_max - T0) / 128); a = fl32(1 / (128 h));
- * base = fl32(fl32(T0 + 128 E) + 128 tau); b = -fl32(base a);
- * u_k = fma32(t_k, a, b); code = clamp(floor(u_k), 0, 7).  The values of the
- * block are then code value * 2^(E8M0 - 127). */
-static void efq_block(const float* t, int nvis, float T0, float a, float t128, uint8_t* codes, uint8_t* scale) {
+ *    tau + j h (j = 1..7): code = #{ j : r_k >= tau + j h }, i.e.
+ *    clamp(floor((r_k - tau) / h), 0, 7); code 7 is E2M1's 6.0.
+ * tau and h are the binary32 parameters of the call.  Every step is exact in
+ * binary64: t_k, T0 are binary32, so t_k - T0, the division by 128, E and
+ * r_k are exact, and tau + j h (j <= 7) needs at most 28 significant bits.
+ * The values of the block are code value * 2^(E8M0 - 127). */
+static void efq_block(const float* t, int nvis, float T0, float tau, float h, uint8_t* codes, uint8_t* scale) {
   for (int i = 0; i < 32; ++i) codes[i] = 0;
   *scale = 0;
   if (nvis <= 0) return;
   float tb = t[0];
   for (int i = 1; i < nvis; ++i)
     if (t[i] > tb) tb = t[i];
-  const float d = tb - T0;
-  const int E = (int)floor((double)d / 128.0);
-  const int s = E - 2 + 127;
+  double E = floor(((double)tb - (double)T0) / 128.0);
+  if (E < -1000.0) E = -1000.0;
+  if (E > 1000.0) E = 1000.0;
+  const int s = (int)E - 2 + 127;
   *scale = (uint8_t)(s < 0 ? 0 : (s > 254 ? 254 : s));
-  const float base = (T0 + (float)(128 * E)) + t128;
-  const float b = -(base * a);
   for (int i = 0; i < nvis; ++i) {
-    const double f = floor((double)fmaf(t[i], a, b));
-    codes[i] = (uint8_t)(f < 0.0 ? 0 : (f > 7.0 ? 7 : (int)f));
+    const double r = ((double)t[i] - (double)T0) / 128.0 - E;
+    int code = 0;
+    for (int j = 1; j <= 7; ++j)
+      if (r >= (double)tau + (double)j * (double)h) code = j;
+    codes[i] = (uint8_t)code;
   }
 }
 
-/* the parameters of R24 in binary32: a = fl32(1 / fl32(128 h)), 128 tau */
-static float efq_slope(double h) { return 1.0f / (128.0f * (float)h); }
-static float efq_t128(double tau) { return 128.0f * (float)tau; }
-
 void fso_efq_block(const float* t, int nvis, float T0, double tau, double h, uint8_t* codes, uint8_t* scale) {
-  efq_block(t, nvis, T0, efq_slope(h), efq_t128(tau), codes, scale);
+  efq_block(t, nvis, T0, (float)tau, (float)h, codes, scale);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -770,13 +769,13 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
     int64_t kb0 = k0, kb1 = k0 + bc < S32 ? k0 + bc : S32;
     if (p->p_mode == FSO_P_EFQ) {
       /* R24: codes straight from the folded scores, block by block */
-      const float a = efq_slope(p->efq_h), t128 = efq_t128(p->efq_tau);
+      const float etau = (float)p->efq_tau, eh = (float)p->efq_h;
       for (int64_t g = kb0 / 32; g < kb1 / 32; ++g) {
         float tf[32];
         int64_t nv = Skv - g * 32;
         int nvis = nv <= 0 ? 0 : (nv >= 32 ? 32 : (int)nv);
         for (int i = 0; i < nvis; ++i) tf[i] = (float)rb->tmp[g * 32 + i];
-        efq_block(tf, nvis, (float)T0, a, t128, rb->pc + g * 32, rb->psc + g);
+        efq_block(tf, nvis, (float)T0, etau, eh, rb->pc + g * 32, rb->psc + g);
         for (int i = 0; i < 32; ++i)
           rb->ph[g * 32 + i] = ldexp(fso_decode(FSO_E2M1, rb->pc[g * 32 + i]), (int)rb->psc[g] - 127);
       }
@@ -922,7 +921,7 @@ static int check_params(const fso_params* p) {
   if (p->kv_tile < 32 || p->kv_tile % 32) return 0;
   if (!(p->tau >= 0.0)) return 0;
   if (p->p_mode == FSO_P_EFQ) {
-    /* R24 works on the binary32 fold with E2M1 P; h in [1/64, 16], |tau| <= 64 */
+    /* R24 takes the binary32 folded scores, with E2M1 P; h in [1/64, 16], |tau| <= 64 */
     if (p->p_elem != FSO_E2M1 || p->fold_mode != FSO_FOLD_FP32) return 0;
     if (!(p->efq_h >= 1.0 / 64.0 && p->efq_h <= 16.0) || !(p->efq_tau >= -64.0 && p->efq_tau <= 64.0)) return 0;
   } else if (p->p_mode != FSO_P_MX && p->p_mode != FSO_P_NONE) {

@@ -121,13 +121,11 @@ uint16_t fso_stage1(float t);
  * R24, EFQ-style direct E2M1 P of one 32-key block ("EFQ-Softmax: Exp-Free
  * Quantization for Softmax", sections II.B-C, III.B): from the block's folded
  * binary32 scores t[0..nvis) (keys nvis..31 absent: code 0; nvis = 0: E8M0 0),
- *   E    = floor(fl32(max t - T0) / 128)      (exponent of the block maximum)
+ * in exact arithmetic, with tau and h rounded to binary32 first:
+ *   l_k  = (t_k - T0) / 128                  (log2 units, reference at T0)
+ *   E    = floor(max l) clamped to [-1000, 1000]  (exponent of the block maximum)
  *   E8M0 = clamp(E - 2 + 127, 0, 254)
- *   a    = fl32(1 / fl32(128 h)),  base = fl32(fl32(T0 + 128 E) + fl32(128 tau)),
- *   b    = -fl32(base a),  u_k = fma32(t_k, a, b),
- *   code = clamp(floor(u_k), 0, 7)           (E2M1 codes 0..7 = 0 .. 6.0)
- * i.e. code = #{j in 1..7 : r_k >= tau + j h} for the residual
- * r_k = (t_k - T0) / 128 - E, up to the binary32 rounding of u_k.
+ *   code = #{j in 1..7 : l_k - E >= tau + j h}   (E2M1 codes 0..7 = 0 .. 6.0)
  */
 void fso_efq_block(const float* t, int nvis, float T0, double tau, double h, uint8_t* codes, uint8_t* scale);
 

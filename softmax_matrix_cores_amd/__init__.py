@@ -34,7 +34,7 @@ ABI_SYMBOLS = (
 # (tau, h) of the EFQ-style E2M1 P rule (fsattn_forward_efq), calibrated offline
 # on synthetic MXFP4 attention by minimizing the output error against exact
 # softmax on the same quantized operands
-EFQ_TAU, EFQ_H = -3.890625, 0.609375
+EFQ_TAU, EFQ_H = -3.875, 0.609375
 
 
 class FsattnError(RuntimeError):

@@ -10,8 +10,9 @@ The pins check the oracle against things fixed by that description and by
 arithmetic, not against its own formula:
 - codes on and just below each threshold, at two block exponents (dyadic
   parameters, so every step is exact);
-- an exact-rational evaluation of the rule on random blocks, away from the
-  rounding boundaries;
+- an exact-rational evaluation of the rule on random blocks, every key;
+- keys exactly on each threshold and one binary32 step below it, with
+  spacings h whose reciprocal has no exact binary32 value;
 - shift invariance: moving a block by whole binades moves only its E8M0;
 - absent keys and empty blocks;
 - end to end: identical keys give O = the mean of V-hat (same P in both
@@ -88,11 +89,35 @@ def test_rule_against_exact_rationals(oracle):
         want, E, dist = rational_rule(t, T0, tau, h)
         assert sc == min(max(E - 2 + 127, 0), 254)
         for i in range(n):
-            if dist[i] > 1e-4:
-                assert codes[i] == want[i], (it, i, l[i], codes[i], want[i])
-                checked += 1
+            assert codes[i] == want[i], (it, i, l[i], codes[i], want[i], dist[i])
+            checked += 1
         assert not codes[n:].any()
     assert checked > 8000
+
+
+@pytest.mark.parametrize("tau,h", [(-3.875, 0.609375), (-3.890625, 0.609375), (-3.25, 0.5625)])
+def test_codes_on_thresholds_with_inexact_slope(oracle, tau, h):
+    """Keys exactly on a threshold tau + j h (binary32 scores) take code j and
+    the next binary32 below takes j - 1, also where 1 / (128 h) has no exact
+    binary32 value (h = 39/64, 9/16): the rule is the threshold count itself,
+    not a rounded slope."""
+    tau32, h32 = np.float32(tau), np.float32(h)
+    for E in (0, -4, 1):
+        t = [T0 + 128 * (E + 0.8)]
+        want = [min(max(math.floor((Fraction(0.8) - Fraction(float(tau32))) / Fraction(float(h32))), 0), 7)]
+        for j in range(1, 8):
+            thr = Fraction(float(T0)) + 128 * (E + Fraction(float(tau32)) + j * Fraction(float(h32)))
+            on = np.float32(float(thr))
+            if Fraction(float(on)) != thr:
+                continue  # the threshold is not a binary32 score
+            t.append(float(on))
+            want.append(j)
+            t.append(float(np.nextafter(on, np.float32(-np.inf))))
+            want.append(j - 1)
+        assert len(t) > 9
+        codes, sc = oracle.efq_block(t, T0, tau, h)
+        assert sc == E - 2 + 127
+        assert list(codes[: len(t)]) == want, (tau, h, E, list(codes[: len(t)]), want)
 
 
 def test_shift_by_whole_binades_moves_only_the_scale(oracle):
