@@ -82,6 +82,8 @@ def lib():
         L.fso_stage1.argtypes = [ctypes.c_float]
         L.fso_efq_block.argtypes = [P, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_double, P, P]
         L.fso_forward.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P, ctypes.c_int64, P, P, P, P, P]
+        L.fso_forward_scores.argtypes = [ctypes.POINTER(Params), ctypes.c_void_p, P, P, P, P, P, P, P,
+                                         ctypes.c_int64, P, P]
         L.fso_forward_masked.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Mask), P, P, P, P, P, P, P,
                                          ctypes.c_int64, P, P, P, P, P]
         L.fso_reference.argtypes = [ctypes.POINTER(Params), ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int64, P]
@@ -232,6 +234,27 @@ def forward(p: Params, q, k, v, rows=None, want_p=False, causal=False, q_lens=No
         out["p_codes"] = pc
         out["p_scales"] = ps
     return out
+
+
+def forward_scores(p: Params, q, k, v, rows, causal=False, q_lens=None, kv_lens=None):
+    """Diagnostics for the given rows: the folded binary32 scores stage 1 sees
+    (after each tile's gate shift; invisible keys left 0) and max_d |Qhat Khat|
+    per (row, key), both [rows, Skv32] (fso_forward_scores; masks as forward)."""
+    rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+    s32 = (p.Skv + 31) // 32 * 32
+    t = np.zeros((len(rows_a), s32), np.float32)
+    a = np.zeros((len(rows_a), s32), np.float64)
+    args = [np.ascontiguousarray(x) for x in (q[0], q[1], k[0], k[1], v[0], v[1])]
+    m = None
+    if causal or q_lens is not None or kv_lens is not None:
+        ql = None if q_lens is None else np.ascontiguousarray(q_lens, dtype=np.int32)
+        kl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
+        m = Mask(1 if causal else 0, _ptr(ql), _ptr(kl))
+    rc = lib().fso_forward_scores(ctypes.byref(p), ctypes.byref(m) if m is not None else None,
+                                  *[_ptr(x) for x in args], _ptr(rows_a), len(rows_a), _ptr(t), _ptr(a))
+    if rc != 0:
+        raise ValueError(f"fso_forward_scores failed ({rc})")
+    return t, a
 
 
 def reference(p: Params, ref: int, q, k, v, rows=None) -> np.ndarray:

@@ -494,6 +494,17 @@ static int dot_terms(const int64_t* qm, const int* qe, const int64_t* km, const 
   return nb;
 }
 
+/* max_d |Qhat_d Khat_d| in binary64 (a diagnostic magnitude, not a score) */
+static double max_prod(const int64_t* qm, const int* qe, const int64_t* km, const int* ke, int D) {
+  double s = 0.0;
+  for (int g = 0; g < D / 32; ++g)
+    for (int j = 0; j < 32; ++j) {
+      const double x = ldexp(fabs((double)qm[g * 32 + j] * (double)km[g * 32 + j]), qe[g] + ke[g]);
+      if (x > s) s = x;
+    }
+  return s;
+}
+
 double fso_folded_score(int qk_elem, const uint8_t* qrow_codes, const uint8_t* qrow_scales,
                         const uint8_t* krow_codes, const uint8_t* krow_scales, int D, double cinit,
                         int exact_fold) {
@@ -598,6 +609,8 @@ typedef struct {
   int32_t* misses; /* R25: per row, tiles the exact rule fires and the shortcut does not */
   uint8_t* pcodes;
   uint8_t* pscales;
+  float* tout;   /* diagnostics: folded scores after the gate shift [rows][S32] */
+  double* aout;  /* diagnostics: max_d |Qhat_d Khat_d| [rows][S32] */
   /* per-head decoded K/V, shared read-only */
   int64_t head;  /* (b*H + h) */
   int64_t* kmint; /* [Skv][D] */
@@ -762,6 +775,13 @@ static void fused_row(job_t* J, int64_t ri, rowbuf_t* rb) {
       for (int d = 0; d < D; ++d) O[d] *= rho;
       l *= rho;
       ++cnt;
+    }
+    if (J->tout) {
+      /* diagnostics: the scores stage 1 sees and their largest products */
+      for (int64_t k = k0; k < k1; ++k) {
+        J->tout[ri * S32 + k] = (float)rb->tmp[k];
+        J->aout[ri * S32 + k] = max_prod(rb->qm, rb->qe, J->kmint + k * D, J->kbexp + k * nbd, D);
+      }
     }
     /* stage 1: folded score -> BF16 pattern (or the exact exponential); the
      * P blocks of the tile run to its end (to S32 on the last tile of the
@@ -934,7 +954,7 @@ static int check_params(const fso_params* p) {
 static int run_rows(const fso_params* p, const fso_mask* mask, int ref, const uint8_t* qc, const uint8_t* qs,
                     const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int64_t* rows,
                     int64_t nrows, double* out_O, double* out_l, int32_t* counts, uint8_t* pcodes,
-                    uint8_t* pscales) {
+                    uint8_t* pscales, float* tout, double* aout) {
   if (!check_params(p)) return FSO_EINVAL;
   int64_t total = (int64_t)p->B * p->H * p->Sq;
   if (!rows) nrows = total;
@@ -947,6 +967,7 @@ static int run_rows(const fso_params* p, const fso_mask* mask, int ref, const ui
   memset(&J, 0, sizeof J);
   J.p = p; J.mask = mask; J.ref = ref; J.qc = qc; J.qs = qs; J.kc = kc; J.ks = ks; J.vc = vc; J.vs = vs;
   J.rows = rows; J.nrows = nrows; J.O = out_O; J.L = out_l; J.counts = counts; J.pcodes = pcodes; J.pscales = pscales;
+  J.tout = tout; J.aout = aout;
   J.misses = p->gate_misses;
   J.kmint = (int64_t*)malloc(sizeof(int64_t) * (size_t)(Skv * D));
   J.kbexp = (int*)malloc(sizeof(int) * (size_t)(Skv * (D / 32)));
@@ -985,21 +1006,35 @@ static int run_rows(const fso_params* p, const fso_mask* mask, int ref, const ui
 int fso_forward(const fso_params* p, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                 const uint8_t* vc, const uint8_t* vs, const int64_t* rows, int64_t nrows, double* out_O,
                 double* out_l, int32_t* counts, uint8_t* p_codes, uint8_t* p_scales) {
-  return run_rows(p, NULL, 0, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, out_l, counts, p_codes, p_scales);
+  return run_rows(p, NULL, 0, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, out_l, counts, p_codes, p_scales, NULL,
+                  NULL);
 }
 
 int fso_forward_masked(const fso_params* p, const fso_mask* m, const uint8_t* qc, const uint8_t* qs,
                        const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs,
                        const int64_t* rows, int64_t nrows, double* out_O, double* out_l, int32_t* counts,
                        uint8_t* p_codes, uint8_t* p_scales) {
-  return run_rows(p, m, 0, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, out_l, counts, p_codes, p_scales);
+  return run_rows(p, m, 0, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, out_l, counts, p_codes, p_scales, NULL,
+                  NULL);
+}
+
+int fso_forward_scores(const fso_params* p, const fso_mask* m, const uint8_t* qc, const uint8_t* qs,
+                       const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs,
+                       const int64_t* rows, int64_t nrows, float* t_out, double* abs_out) {
+  if (!t_out || !abs_out) return FSO_EINVAL;
+  int64_t n = rows ? nrows : (int64_t)p->B * p->H * p->Sq;
+  double* O = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)p->D);
+  if (!O) return FSO_ENOMEM;
+  int rc = run_rows(p, m, 0, qc, qs, kc, ks, vc, vs, rows, nrows, O, NULL, NULL, NULL, NULL, t_out, abs_out);
+  free(O);
+  return rc;
 }
 
 int fso_reference(const fso_params* p, int ref, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                   const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int64_t* rows, int64_t nrows,
                   double* out_O) {
   if (ref < FSO_REF_R1 || ref > FSO_REF_R3) return FSO_EINVAL;
-  return run_rows(p, NULL, ref, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, NULL, NULL, NULL, NULL);
+  return run_rows(p, NULL, ref, qc, qs, kc, ks, vc, vs, rows, nrows, out_O, NULL, NULL, NULL, NULL, NULL, NULL);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -164,9 +164,9 @@ int fso_forward(const fso_params* p,
                 uint8_t* p_codes, uint8_t* p_scales);
 
 /*
- * Masked and variable-length attention (the pages put masks before the
- * score shift and probability generation: "Fused softmax makes quantized
- * attention faster on AMD GPUs", section "What the evidence shows").
+ * Masked and variable-length attention (masks go before the score shift and
+ * probability generation: "EFQ-Softmax: Exp-Free Quantization for Softmax",
+ * section III.D "Algorithmic Cost and Method Boundary", kernel boundary).
  *  causal   query i of batch b sees key k only if k <= i + kv_len_b - q_len_b
  *           (queries aligned to the end of the keys)
  *  q_lens   optional host [B]: valid queries per batch, clamped to [0, Sq]
@@ -188,6 +188,18 @@ int fso_forward_masked(const fso_params* p, const fso_mask* m,
                        const int64_t* rows, int64_t nrows,
                        double* out_O, double* out_l, int32_t* counts,
                        uint8_t* p_codes, uint8_t* p_scales);
+
+/*
+ * Diagnostics of the forward for rows[0..nrows) (all rows if rows is NULL):
+ * t_out [rows][Skv32] the folded binary32 score of each visible key after its
+ * tile's gate shift (the value stage 1 floors; other keys untouched), abs_out
+ * [rows][Skv32] max_d |Qhat_d Khat_d| in binary64, the magnitude the rounding
+ * of a matrix core that does not return the exactly rounded sum scales with.  m may be NULL.  Used to explain P-code differences of such hardware.
+ */
+int fso_forward_scores(const fso_params* p, const fso_mask* m, const uint8_t* qc, const uint8_t* qs,
+                       const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs,
+                       const int64_t* rows, int64_t nrows, float* t_out, double* abs_out);
+
 
 /* References on the same quantized operands (see FSO_REF_*). */
 int fso_reference(const fso_params* p, int ref,

@@ -65,7 +65,7 @@ def same_bytes(gpu: fs.MXTensor, ora, axis: int = 0) -> tuple[bool, bool]:
     return np.array_equal(gc, ora[0].ravel()), np.array_equal(gs4, os_)
 
 
-def oracle_params(O, w: W.Workload, tau=None, kv_tile=None, efq=None, gate="exact"):
+def oracle_params(O, w: W.Workload, tau=None, kv_tile=None, efq=None, gate="exact", c=0.0):
     """efq = (tau, h): E2M1 P by the EFQ-style rule (p_mode P_EFQ); gate "pattern":
     the stage-1 pattern gate shortcut (gate_mode GATE_PATTERN)."""
     kw = {} if efq is None else dict(p_mode=O.P_EFQ, efq_tau=efq[0], efq_h=efq[1])
@@ -73,7 +73,7 @@ def oracle_params(O, w: W.Workload, tau=None, kv_tile=None, efq=None, gate="exac
         kw["gate_mode"] = O.GATE_PATTERN
     return O.make_params(w.B, w.H, w.Sq, w.Skv, w.D, O.ELEM_NAMES[w.qk_elem], O.ELEM_NAMES[w.v_elem],
                          O.ELEM_NAMES[w.p_elem], tau=w.tau if tau is None else tau,
-                         kv_tile=w.kv_tile if kv_tile is None else kv_tile, **kw)
+                         kv_tile=w.kv_tile if kv_tile is None else kv_tile, c=c, **kw)
 
 
 def rel_frob(a: np.ndarray, b: np.ndarray) -> float:
@@ -89,10 +89,14 @@ def p_mismatch(gc, gs, oc, os_) -> float:
 
 
 def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=None, kv_tile=None,
-             check_quant=True, causal=False, q_lens=None, kv_lens=None, efq=None, gate="exact"):
+             check_quant=True, causal=False, q_lens=None, kv_lens=None, efq=None, gate="exact", c=0.0,
+             more_dumps=()):
     """Full comparison on workload w.  rows: oracle row sample (None = all rows).
     causal / q_lens / kv_lens: masks ([B] lists), sent to both sides.
     efq = (tau, h) for E2M1 P (default: the library's calibrated pair).
+    c: the Schraudolph shift (both sides).
+    more_dumps: further P-dump windows (b, h, row0, row1), each from a launch
+    of its own on the same operands; their P codes join the comparison.
     Returns a dict of metrics; asserts nothing."""
     masked = causal or q_lens is not None or kv_lens is not None
     if w.p_elem == "e2m1" and efq is None:
@@ -100,7 +104,8 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
     log(f"[case] {w.name} B={w.B} H={w.H} Sq={w.Sq} Skv={w.Skv} D={w.D} {w.qk_elem}/{w.v_elem}/{w.p_elem} "
         f"tau={w.tau if tau is None else tau} kv_tile={w.kv_tile if kv_tile is None else kv_tile}"
         + (f" causal={causal} q_lens={q_lens} kv_lens={kv_lens}" if masked else "")
-        + (f" efq={efq}" if efq is not None else "") + (f" gate={gate}" if gate != "exact" else ""))
+        + (f" efq={efq}" if efq is not None else "") + (f" gate={gate}" if gate != "exact" else "")
+        + (f" c={c}" if c else ""))
     q, k, v = (x.cpu() for x in W.make_inputs(w, device="cuda:0"))
     tau_ = w.tau if tau is None else tau
     kvt = w.kv_tile if kv_tile is None else kv_tile
@@ -126,8 +131,18 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
     if gate != "exact":
         mk["gate"] = gate
     out = fs.forward(Qg, Kg, Vg, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=tau_, kv_tile=kvt,
-                     counts=counts, p_dump=pd, **mk)
+                     counts=counts, p_dump=pd, c=c, **mk)
     torch.cuda.synchronize()
+    windows = []  # (b, h, r0, r1, gpu codes, gpu scales)
+    if pd is not None:
+        windows.append((pd[0], pd[1], pd[2], pd[3], pd[4].cpu().numpy(), pd[5].cpu().numpy()))
+    for (b, h, r0, r1) in more_dumps:
+        pc = torch.zeros(r1 - r0, s32, dtype=torch.uint8, device="cuda:0")
+        ps = torch.zeros(r1 - r0, s32 // 32, dtype=torch.uint8, device="cuda:0")
+        fs.forward(Qg, Kg, Vg, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=tau_, kv_tile=kvt,
+                   p_dump=(b, h, r0, r1, pc, ps), c=c, **mk)
+        torch.cuda.synchronize()
+        windows.append((b, h, r0, r1, pc.cpu().numpy(), ps.cpu().numpy()))
     log(f"[case] {w.name}: GPU done")
     # oracle
     Qo, Ko, Vo = oracle_quant(O, q, k, v, w)
@@ -135,7 +150,7 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
         res["quant_q"] = same_bytes(Qg, Qo)
         res["quant_k"] = same_bytes(Kg, Ko)
         res["quant_v"] = same_bytes(Vg, Vo, axis=1)
-    p = oracle_params(O, w, tau=tau_, kv_tile=kvt, efq=efq, gate=gate)
+    p = oracle_params(O, w, tau=tau_, kv_tile=kvt, efq=efq, gate=gate, c=c)
     row_ids = None if rows is None else np.asarray(rows, dtype=np.int64)
     omk = dict(causal=causal, q_lens=q_lens, kv_lens=kv_lens) if masked else {}
     r = O.forward(p, Qo, Ko, Vo, rows=row_ids, **omk)
@@ -154,11 +169,20 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
         dead = r["l"] == 0
         res["dead_rows"] = int(dead.sum())
         res["dead_rows_nonzero"] = int((gout[dead] != 0).any(axis=1).sum()) + int((gcnt[dead] != 0).sum())
-    if dump_rows is not None:
-        b, h, r0, r1 = pd[:4]
-        drows = (b * w.H + h) * w.Sq + np.arange(r0, r1)
+    if windows:
+        drows = np.concatenate([(b * w.H + h) * w.Sq + np.arange(r0, r1) for b, h, r0, r1, _, _ in windows])
+        gc = np.concatenate([x[4] for x in windows])
+        gs = np.concatenate([x[5] for x in windows])
         rd = O.forward(p, Qo, Ko, Vo, rows=drows, want_p=True, **omk)
-        res["p_mismatch"] = p_mismatch(pd[4].cpu().numpy(), pd[5].cpu().numpy(), rd["p_codes"], rd["p_scales"])
+        res["p_rows"] = int(len(drows))
+        res["p_mismatch"] = p_mismatch(gc, gs, rd["p_codes"], rd["p_scales"])
+        if res["p_mismatch"] > P_MISMATCH_TOL and w.qk_elem == "e4m3" and efq is None:
+            t, _ = O.forward_scores(p, Qo, Ko, Vo, drows, **omk)
+            steps = []
+            res["p_bad"], res["p_unexplained"] = explain_fp8(O, O.ELEM_NAMES[w.p_elem], gc, gs, rd["p_codes"],
+                                                             rd["p_scales"], t, w.D, steps)
+            if steps:
+                res["p_flip_steps_max"] = max(steps)
     log(f"[case] {w.name}: {res}")
     return res
 
@@ -177,18 +201,82 @@ def assert_ok(res: dict, defer_p: bool = False):
         check_p(res)
 
 
+# FP8 (E4M3) score products: the matrix core does not return the correctly
+# rounded sum on gfx950.  In the fused kernel, whose accumulator starts at the
+# folded offset (about 2^14), the score error measured through the P codes of
+# the 4096-key FP8 workload (15 832 code flips) is symmetric and reaches 124
+# binary32 steps of t at D = 128: fp8_bound allows D steps, one per product.
+# A P code that differs from the oracle's is explained when the oracle's
+# folded score t lies within that bound of an integer n and the two codes are
+# those of the BF16 patterns n - 1 and n (a floor on the other side of n); a
+# block scale, when one score of its block lies so close to the pattern at
+# which the E8M0 steps between the two values.  FP8 cases whose P-code
+# mismatch exceeds the criterion are reported as expected failures only if
+# the excess stays below FP8_XFAIL_LIMIT and every differing element is so
+# explained; otherwise they fail.  The criterion itself is not met for them.
+FP8_XFAIL_LIMIT = 1.5e-3
+
+
+def fp8_bound(t, D: int):
+    """D binary32 steps of each folded score."""
+    return D * np.spacing(np.abs(np.asarray(t, np.float32))).astype(np.float64)
+
+
+def _bf16_val(b: int) -> float:
+    return 0.0 if b < 128 else float(np.array([b << 16], np.uint32).view(np.float32)[0])
+
+
+def _scale_step(O, pe: int, hi: int) -> int:
+    """Smallest BF16 pattern b whose fit-max E8M0 (as a P block max) is >= hi."""
+    lo, up = 128, 0x7F7F
+    while lo < up:
+        mid = (lo + up) // 2
+        if O.scale_code(pe, O.SCALE_FITMAX, _bf16_val(mid)) >= hi:
+            up = mid
+        else:
+            lo = mid + 1
+    return lo
+
+
+def explain_fp8(O, pe: int, gc, gs, oc, os_, t, D: int, steps=None) -> tuple[int, int]:
+    """(mismatching elements, unexplained elements) of a P dump against the oracle.
+    steps: optional list receiving |t - n| / ulp32(t) of every code flip whose
+    two codes are those of the patterns n - 1 and n (the data behind the bound)."""
+    S32 = gc.shape[1]
+    gse = np.repeat(gs, 32, axis=1)[:, :S32]
+    ose = np.repeat(os_, 32, axis=1)[:, :S32]
+    bad = (gc != oc) | (gse != ose)
+    bound = fp8_bound(t, D)
+    unexplained = 0
+    for r, g in np.argwhere(gs != os_):
+        keys = slice(32 * g, 32 * g + 32)
+        ok = abs(int(gs[r, g]) - int(os_[r, g])) == 1
+        if ok:
+            bT = _scale_step(O, pe, max(int(gs[r, g]), int(os_[r, g])))
+            ok = bool((np.abs(t[r, keys].astype(np.float64) - bT) <= bound[r, keys]).any())
+        if not ok:
+            unexplained += int(bad[r, keys].sum())
+    for r, k in np.argwhere((gc != oc) & (gse == ose)):
+        n = int(np.rint(t[r, k]))
+        X = 2.0 ** (int(ose[r, k]) - 127)
+        codes = {O.encode(pe, _bf16_val(b) / X) for b in (n - 1, n)}
+        adjacent = codes == {int(gc[r, k]), int(oc[r, k])}
+        e = abs(float(t[r, k]) - n)
+        if adjacent and steps is not None:
+            steps.append(e / float(np.spacing(np.float32(abs(t[r, k])))))
+        if not (adjacent and e <= bound[r, k]):
+            unexplained += 1
+    return int(bad.sum()), unexplained
+
+
 def check_p(res: dict):
-    """P-code mismatch <= 1e-3.  With FP8 (E4M3) Q/K the score products come
-    from the matrix core, which does not return the correctly rounded sum for
-    FP8 operands on gfx950 (a probe of the scaled FP8 products finds 7-85 % of
-    results exact, depending on shape and active K, against 100 % for FP6 and
-    FP4).  floor(t) then differs from the oracle's where t lies within a few
-    hundredths of an integer; an excess over 1e-3 in that case is reported as
-    an expected failure, after every other criterion has passed."""
+    """P-code mismatch <= 1e-3; for FP8 Q/K see explain_fp8 above."""
     if "p_mismatch" not in res or res["p_mismatch"] <= P_MISMATCH_TOL:
         return
-    if res.get("qk_elem") == "e4m3":
-        import pytest
-        pytest.xfail(f"FP8 score products are inexact on the matrix core: P-code mismatch "
-                     f"{res['p_mismatch']:.4g} > {P_MISMATCH_TOL}")
+    if res.get("qk_elem") == "e4m3" and "p_unexplained" in res:
+        if res["p_mismatch"] <= FP8_XFAIL_LIMIT and res["p_unexplained"] == 0:
+            import pytest
+            pytest.xfail(f"P-code criterion not met: FP8 score products are inexact on the matrix core; "
+                         f"mismatch {res['p_mismatch']:.4g} > {P_MISMATCH_TOL}, all {res['p_bad']} differing "
+                         f"elements explained by the products' rounding")
     raise AssertionError(res)

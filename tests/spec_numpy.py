@@ -204,11 +204,12 @@ def references(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int)
 
 
 def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, tau: float = 8.0,
-            kv_tile: int = 64, c: float = 0.0, visible=None):
+            kv_tile: int = 64, c: float = 0.0, visible=None, t_out=None):
     """Tiny forward for one head.  qb [Sq,D], kb/vb [Skv,D] uint16 bf16 bit patterns.
     visible: optional [Sq] number of keys row i sees (keys 0 .. visible[i]-1);
     the others are absent (no part in any maximum, P = 0); a row that sees no
-    key gives O = 0.
+    key gives O = 0.  t_out: optional [Sq, Skv] array receiving the folded
+    scores stage 1 sees (after each tile's gate shift).
     Returns (O [Sq,D] float, counts [Sq], P codes [Sq,Skv32], P scales [Sq,Skv32/32])."""
     Sq, D = qb.shape
     Skv = kb.shape[0]
@@ -246,6 +247,9 @@ def forward(qb, kb, vb, sigma: float, qk_elem: int, v_elem: int, p_elem: int, ta
                     num = [x * Fraction(rho) for x in num]
                     den = den * Fraction(rho)
                     counts[i] += 1
+            if t_out is not None:
+                for k in ks:
+                    t_out[i, k] = float(t[k])
             # stage 1 (integer part of the folded score as a BF16 pattern) and stage 2 (MX)
             hi = min((j + 1) * kv_tile, S32)
             pvals = {}
