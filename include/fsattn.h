@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define FSATTN_ABI_VERSION 1
+#define FSATTN_ABI_VERSION 2
 
 typedef enum {
   FSATTN_OK = 0,
@@ -89,6 +89,18 @@ const char* fsattn_status_str(int status);
  */
 int64_t fsattn_mx_codes_bytes(int elem, int64_t n_mat, int64_t rows, int64_t cols, int block_axis);
 int64_t fsattn_mx_scales_bytes(int64_t n_mat, int64_t rows, int64_t cols, int block_axis);
+
+/*
+ * fsattn_fold_prescale -- the multiplicative part of the fold: fl32(128 *
+ * log2(e) * softmax_scale), the product taken in binary64 and rounded once.
+ * Scores of Q-hat . K-hat are then BF16 bit-pattern units of the Schraudolph
+ * exponential ("Fused-Softmax shifts an AI attention bottleneck onto faster
+ * GPU hardware", paragraph 6: its linear transform is folded into the score
+ * product).  Pass the result as fsattn_quantize_mx's prescale for Q; the
+ * forward checks it against softmax_scale.  Host-only.  Returns NaN when
+ * softmax_scale is not a positive finite number.
+ */
+float fsattn_fold_prescale(float softmax_scale);
 
 /*
  * fsattn_quantize_mx -- MX-quantize a bf16 tensor (Q, K or V).
@@ -153,11 +165,16 @@ typedef struct {
   int Sq, Skv;           /* query and key counts (>= 1 for Skv, any length: tails are masked) */
   int D;                 /* head dimension: 64 or 128 */
   float softmax_scale;   /* sigma; must equal q->prescale / (128 log2 e) to within 2 ulp */
-  int p_elem;            /* element format of P: E4M3 or E2M3 (E2M1: fsattn_forward_efq only) */
+  int p_elem;            /* element format of P: E4M3, E2M3 or E3M2 (E2M1: fsattn_forward_efq only) */
+  int p_scale_rule;      /* E8M0 rule of P's blocks: FSATTN_SCALE_FITMAX (the kernels implement only
+                            this rule; FSATTN_SCALE_OCP_FLOOR returns FSATTN_E_UNSUPPORTED).  The
+                            operands may be quantized with either rule: the forward reads their codes
+                            and scales as they are */
   float tau;             /* rollback threshold in log2 units of P, >= 0 (default 8); keep it below
                             128 - c/128: above, accepted scores can pass the stage-1 clamp */
   float schraudolph_c;   /* shift c in BF16-pattern units (default 0) */
-  int kv_tile;           /* keys per gate tile: 64 or 128 */
+  int kv_tile;           /* keys per gate tile, a positive multiple of 32; the kernels run 64 and 128
+                            (other multiples of 32 return FSATTN_E_UNSUPPORTED) */
   int32_t* rollback_counts; /* optional device [B][H][Sq]: fires per query row; NULL = not written */
   uint8_t* p_dump_codes;    /* optional device [(p_row1-p_row0)][Skv32], one code per key, for rows
                                [p_row0, p_row1) of head (p_b, p_h); NULL = no dump */
@@ -183,9 +200,10 @@ typedef struct {
  *   stage 1: b = floor(t) as a BF16 bit pattern (0 if t < 128, at most 0x7F7F)
  *   stage 2: P = MX(bf16(b)) per 32 consecutive keys (fit-max E8M0)
  *   O_i += P V, l_i += P 1 (same P); finally O_i / l_i rounded to bf16.
- * Errors: FSATTN_E_INVALID_ARG (null, sizes, D not 64/128, kv_tile not
- * 64/128, tau < 0, prescale/softmax_scale mismatch, bad dump window),
- * FSATTN_E_UNSUPPORTED (format combination, Skv * D > 2^30),
+ * Errors: FSATTN_E_INVALID_ARG (null, sizes, D not 64/128, kv_tile not a
+ * positive multiple of 32, tau < 0, bad enum, prescale/softmax_scale
+ * mismatch, bad dump window), FSATTN_E_UNSUPPORTED (format combination,
+ * kv_tile other than 64 or 128, P scale rule OCP_FLOOR, Skv * D > 2^30),
  * FSATTN_E_ALIGNMENT (codes not 16-byte, K or V scales not 4-byte, out not
  * 4-byte aligned), FSATTN_E_HIP.
  */
@@ -194,10 +212,11 @@ int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsat
 
 /*
  * fsattn_forward_masked -- fsattn_forward with causal and variable-length
- * masks.  The pages apply masks before the score shift and probability
- * generation ("Fused softmax makes quantized attention faster on AMD GPUs",
- * chiosa.app, section "What the evidence shows"): a masked key takes no part
- * in any tile maximum (tile-0 reference, rollback gate) and its P is 0.
+ * masks.  Masks are applied before the score shift and probability
+ * generation ("EFQ-Softmax: Exp-Free Quantization for Softmax", section
+ * III.D "Algorithmic Cost and Method Boundary", kernel boundary): a masked
+ * key takes no part in any tile maximum (tile-0 reference, rollback gate) and
+ * its P is 0.
  * Tiles keep their positions (tile j = keys [j*kv_tile, (j+1)*kv_tile)).
  *
  * mask (may be NULL = no mask, the same as fsattn_forward):
@@ -239,11 +258,12 @@ int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const
  *   E8M0 = clamp(E - 2 + 127, 0, 254)
  *   code = #{ j in 1..7 : l - E >= efq_tau + j efq_h }   (code 7 is E2M1's 6.0)
  * i.e. the residual l - E is compared with uniformly spaced thresholds.  The
- * kernel evaluates the comparison as clamp(floor(fma32(t, a, b)), 0, 7) with
- * a = fl32(1 / fl32(128 efq_h)) and b = -fl32(fl32(fl32(T0 + 128 E) +
- * 128 efq_tau) a); where 1 / (128 efq_h) is not a binary32 value this can
- * differ from the exact count for scores within about 2^-16 of a threshold
- * (a P-code difference, inside the method's P-code tolerance).  Masked keys
+ * kernel counts them as clamp(floor((t - base) a), 0, 7) with the exact
+ * base = T0 + 128 E + 128 efq_tau and a = 1 / (128 efq_h) rounded up to
+ * binary32.  A score exactly on a threshold gets the higher code.  For the
+ * calibrated spacing (128 efq_h = 78) the count is exact for every t >= 1024
+ * (binary32 step 2^-13 or coarser); for other spacings, or smaller t, a score
+ * a few binary32 steps below a threshold may also get it.  Masked keys
  * get code 0.  (efq_tau, efq_h) are calibrated offline; -3.875 and
  * 0.609375 minimize the output error on synthetic MXFP4 attention.
  *
@@ -301,8 +321,8 @@ int fsattn_forward_bf16_baseline(const void* q, const void* k, const void* v, in
  * = fsattn_forward_bf16_baseline): each row's softmax runs over its visible
  * keys; rows that see no key, and rows past q_len, are stored as 0.  The
  * comparison point for masked fused attention (masks precede the softmax,
- * "Fused softmax makes quantized attention faster on AMD GPUs", section "What
- * the evidence shows").  Errors as fsattn_forward_bf16_baseline, plus
+ * "EFQ-Softmax: Exp-Free Quantization for Softmax", section III.D
+ * "Algorithmic Cost and Method Boundary", kernel boundary).  Errors as fsattn_forward_bf16_baseline, plus
  * FSATTN_E_INVALID_ARG if causal is not 0/1 and FSATTN_E_ALIGNMENT if a
  * length array is not 4-byte aligned.
  */
@@ -322,12 +342,15 @@ int fsattn_forward_bf16_baseline_masked(const void* q, const void* k, const void
  * constant-rate counter (s_memrealtime, the device's wall-clock rate) at
  * start and end, so the caller can derive the matrix-core rate and the
  * shader clock under that load.  stamps: caller-owned device
- * uint64 [workgroups][4], 8-byte aligned.
+ * uint64 [workgroups][4], 8-byte aligned.  wall_clock_khz: optional host
+ * int, set to the constant rate of the second counter (kHz) of the current
+ * device.
  * Errors: FSATTN_E_INVALID_ARG (fmt, iters outside [1, 2^32], workgroups
  * outside [1, 2^20], stamps NULL), FSATTN_E_ALIGNMENT, FSATTN_E_HIP.
  */
 #define FSATTN_PROBE_BF16 16
-int fsattn_probe_mfma(int fmt, int64_t iters, int workgroups, unsigned long long* stamps, void* stream);
+int fsattn_probe_mfma(int fmt, int64_t iters, int workgroups, unsigned long long* stamps, int* wall_clock_khz,
+                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,6 @@ fallback: if the library is missing, calls raise.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -28,7 +27,7 @@ ABI_SYMBOLS = (
     "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
     "fsattn_quantize_mx", "fsattn_quantize_mx_rmsnorm", "fsattn_forward", "fsattn_forward_masked",
     "fsattn_forward_bf16_baseline", "fsattn_forward_bf16_baseline_masked", "fsattn_forward_efq",
-    "fsattn_pattern_gate_tau", "fsattn_probe_mfma",
+    "fsattn_pattern_gate_tau", "fsattn_probe_mfma", "fsattn_fold_prescale",
 )
 
 # (tau, h) of the EFQ-style E2M1 P rule (fsattn_forward_efq), calibrated offline
@@ -52,7 +51,8 @@ class _MxTensor(ctypes.Structure):
 class _Params(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int), ("H", ctypes.c_int), ("Sq", ctypes.c_int), ("Skv", ctypes.c_int), ("D", ctypes.c_int),
-        ("softmax_scale", ctypes.c_float), ("p_elem", ctypes.c_int), ("tau", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float), ("p_elem", ctypes.c_int), ("p_scale_rule", ctypes.c_int),
+        ("tau", ctypes.c_float),
         ("schraudolph_c", ctypes.c_float), ("kv_tile", ctypes.c_int),
         ("rollback_counts", ctypes.c_void_p), ("p_dump_codes", ctypes.c_void_p), ("p_dump_scales", ctypes.c_void_p),
         ("p_b", ctypes.c_int), ("p_h", ctypes.c_int), ("p_row0", ctypes.c_int), ("p_row1", ctypes.c_int),
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         V, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.fsattn_abi_version.restype = I
+        L.fsattn_fold_prescale.restype = ctypes.c_float
+        L.fsattn_fold_prescale.argtypes = [ctypes.c_float]
         L.fsattn_status_str.restype = ctypes.c_char_p
         L.fsattn_status_str.argtypes = [I]
         L.fsattn_mx_codes_bytes.restype = I64
@@ -100,7 +102,7 @@ def lib() -> ctypes.CDLL:
         L.fsattn_pattern_gate_tau.restype = I
         L.fsattn_pattern_gate_tau.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_float)]
         L.fsattn_probe_mfma.restype = I
-        L.fsattn_probe_mfma.argtypes = [I, I64, I, V, V]
+        L.fsattn_probe_mfma.argtypes = [I, I64, I, V, ctypes.POINTER(ctypes.c_int), V]
         L.fsattn_forward_bf16_baseline.restype = I
         L.fsattn_forward_bf16_baseline.argtypes = [V, V, V, I, I, I, I, I, ctypes.c_float, V, V]
         L.fsattn_forward_bf16_baseline_masked.restype = I
@@ -126,8 +128,26 @@ def _check(fn: str, status: int):
 
 
 def fold_prescale(softmax_scale: float) -> float:
-    """fl32(128 * log2(e) * softmax_scale): the multiplicative part of the fold."""
-    return float(torch.tensor(128.0 * math.log2(math.e) * softmax_scale, dtype=torch.float64).float())
+    """fl32(128 * log2(e) * softmax_scale): the multiplicative part of the fold (fsattn_fold_prescale)."""
+    v = lib().fsattn_fold_prescale(ctypes.c_float(softmax_scale))
+    if v != v:
+        raise ValueError(f"softmax_scale must be positive and finite, got {softmax_scale}")
+    return float(v)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, numel: int, device: torch.device):
+    """Check a buffer before its pointer goes to the library, which has no size
+    information: dtype, device, contiguity and at least `numel` elements."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {numel}")
 
 
 @dataclass
@@ -212,25 +232,42 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
             p_elem, tau: float = 8.0, c: float = 0.0, kv_tile: int = 64, counts: torch.Tensor | None = None,
             out: torch.Tensor | None = None, p_dump: tuple | None = None, stream=None, causal: bool = False,
             q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None, efq_tau: float = EFQ_TAU,
-            efq_h: float = EFQ_H, gate: str = "exact") -> torch.Tensor:
+            efq_h: float = EFQ_H, gate: str = "exact", p_scale_rule: int = SCALE_FITMAX) -> torch.Tensor:
     """Fused-Softmax attention forward.  Returns bf16 [B,H,Sq,D].
     counts: optional int32 [B,H,Sq] written with rollback counts.
     p_dump: optional (b, h, row0, row1, codes uint8 [rows, Skv32], scales uint8 [rows, Skv32/32]).
     causal / q_lens / kv_lens: masks (fsattn_forward_masked); lens are device int32 [B].
     p_elem "e2m1": P straight from the scores by the EFQ-style rule with (efq_tau, efq_h)
     (fsattn_forward_efq).
-    gate "pattern": the gate shortcut on stage-1 patterns (fsattn_pattern_gate_tau)."""
+    gate "pattern": the gate shortcut on stage-1 patterns (fsattn_pattern_gate_tau).
+    Every buffer is checked (dtype, device, contiguity, size) before the call."""
     dev = Q.codes.device
     if gate == "pattern":
         tau = pattern_gate_tau(tau, c)
     elif gate != "exact":
         raise ValueError(f"unknown gate {gate!r}")
+    if min(B, H, Sq) < 0 or Skv < 1 or D not in (64, 128):
+        raise ValueError(f"bad shape B={B} H={H} Sq={Sq} Skv={Skv} D={D}")
+    # the library sees raw pointers only: every buffer is checked here against
+    # the sizes the shapes imply
+    for X, name, rows, axis in ((Q, "Q", Sq, 0), (K, "K", Skv, 0), (V, "V", Skv, 1)):
+        cb, sb = mx_sizes(X.elem, B * H, rows, D, axis)
+        _need(X.codes, name + ".codes", torch.uint8, cb, dev)
+        _need(X.scales, name + ".scales", torch.uint8, sb, dev)
     if out is None:
         out = torch.empty(B, H, Sq, D, dtype=torch.bfloat16, device=dev)
-    p = _Params(B, H, Sq, Skv, D, softmax_scale, _elem(p_elem), tau, c, kv_tile,
+    _need(out, "out", torch.bfloat16, B * H * Sq * D, dev)
+    if counts is not None:
+        _need(counts, "counts", torch.int32, B * H * Sq, dev)
+    p = _Params(B, H, Sq, Skv, D, softmax_scale, _elem(p_elem), p_scale_rule, tau, c, kv_tile,
                 counts.data_ptr() if counts is not None else None, None, None, 0, 0, 0, 0)
     if p_dump is not None:
         b, h, r0, r1, pc, ps = p_dump
+        if not (0 <= b < B and 0 <= h < H and 0 <= r0 < r1 <= Sq):
+            raise ValueError(f"bad P dump window {(b, h, r0, r1)}")
+        s32 = (Skv + 31) // 32 * 32
+        _need(pc, "p_dump codes", torch.uint8, (r1 - r0) * s32, dev)
+        _need(ps, "p_dump scales", torch.uint8, (r1 - r0) * (s32 // 32), dev)
         p.p_dump_codes, p.p_dump_scales = pc.data_ptr(), ps.data_ptr()
         p.p_b, p.p_h, p.p_row0, p.p_row1 = b, h, r0, r1
     q, k, v = Q._c(), K._c(), V._c()
@@ -272,10 +309,17 @@ def forward_bf16_baseline(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sof
                           q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None) -> torch.Tensor:
     """Conventional BF16 attention forward (online softmax).  q [B,H,Sq,D], k/v [B,H,Skv,D].
     causal / q_lens / kv_lens: the masks of forward() (fsattn_forward_bf16_baseline_masked)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
     B, H, Sq, D = q.shape
     Skv = k.shape[2]
+    if k.shape != (B, H, Skv, D) or v.shape != (B, H, Skv, D):
+        raise ValueError(f"k and v must be [B, H, Skv, D] matching q {tuple(q.shape)}")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, t.numel(), q.device)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, q.numel(), q.device)
     if causal or q_lens is not None or kv_lens is not None:
         for t in (q_lens, kv_lens):
             if t is not None and (t.dtype != torch.int32 or t.device != q.device or t.shape != (B,) or
@@ -297,12 +341,14 @@ def forward_bf16_baseline(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sof
 PROBE_BF16 = 16
 
 
-def probe_mfma(fmt, iters: int, workgroups: int, stream=None) -> torch.Tensor:
+def probe_mfma(fmt, iters: int, workgroups: int, stream=None) -> tuple[torch.Tensor, int]:
     """Run the pure matrix-product kernel (fsattn_probe_mfma); returns the device
-    int64 stamps [workgroups, 4] (shader clock start/end, wall clock start/end).
-    fmt: an MX element name / code, or "bf16"."""
+    int64 stamps [workgroups, 4] (shader clock start/end, constant-rate counter
+    start/end) and that counter's rate in kHz.  fmt: an MX element name / code,
+    or "bf16"."""
     f = PROBE_BF16 if fmt == "bf16" else _elem(fmt)
     stamps = torch.zeros(workgroups, 4, dtype=torch.int64, device="cuda")
+    khz = ctypes.c_int(0)
     _check("fsattn_probe_mfma", lib().fsattn_probe_mfma(f, int(iters), int(workgroups), stamps.data_ptr(),
-                                                        _stream(stream)))
-    return stamps
+                                                        ctypes.byref(khz), _stream(stream)))
+    return stamps, int(khz.value)

@@ -34,6 +34,9 @@ int64_t nblocks(int64_t n_mat, int64_t rows, int64_t cols, int axis) {
 // fl32(128 * log2(e) * sigma): the multiplicative part of the fold
 float fold_prescale(float sigma) { return (float)(128.0 * 1.4426950408889634 * (double)sigma); }
 
+// FP6 formats of P the two-stage conversion produces
+bool six_bit(int e) { return e == FSATTN_E2M3 || e == FSATTN_E3M2; }
+
 bool within_ulps(float a, float b, int ulps) {
   int32_t ia, ib;
   __builtin_memcpy(&ia, &a, 4);
@@ -48,6 +51,11 @@ bool within_ulps(float a, float b, int ulps) {
 extern "C" {
 
 int fsattn_abi_version(void) { return FSATTN_ABI_VERSION; }
+
+float fsattn_fold_prescale(float softmax_scale) {
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return NAN;
+  return fold_prescale(softmax_scale);
+}
 
 const char* fsattn_status_str(int s) {
   switch (s) {
@@ -135,7 +143,8 @@ static int forward_impl(const fsattn_params* p, const fsattn_mask* mask, bool ef
   }
   if (p->B < 0 || p->H < 0 || p->Sq < 0 || p->Skv < 1) return FSATTN_E_INVALID_ARG;
   if (p->D != 64 && p->D != 128) return FSATTN_E_INVALID_ARG;
-  if (p->kv_tile != 64 && p->kv_tile != 128) return FSATTN_E_INVALID_ARG;
+  if (p->kv_tile < 32 || p->kv_tile % 32) return FSATTN_E_INVALID_ARG;
+  if (p->p_scale_rule != FSATTN_SCALE_FITMAX && p->p_scale_rule != FSATTN_SCALE_OCP_FLOOR) return FSATTN_E_INVALID_ARG;
   if (!(p->tau >= 0.0f) || !isfinite(p->tau) || !isfinite(p->schraudolph_c)) return FSATTN_E_INVALID_ARG;
   if (!(p->softmax_scale > 0.0f) || !isfinite(p->softmax_scale)) return FSATTN_E_INVALID_ARG;
   if (!elem_bits(q->elem) || !elem_bits(v->elem) || !elem_bits(p->p_elem)) return FSATTN_E_INVALID_ARG;
@@ -143,6 +152,9 @@ static int forward_impl(const fsattn_params* p, const fsattn_mask* mask, bool ef
   if (!within_ulps(q->prescale, fold_prescale(p->softmax_scale), 2)) return FSATTN_E_INVALID_ARG;
   if (k->prescale != 1.0f || v->prescale != 1.0f) return FSATTN_E_INVALID_ARG;
   if (!fsattn::fwd_supported(q->elem, v->elem, p->p_elem)) return FSATTN_E_UNSUPPORTED;
+  // the kernels run 64- and 128-key gate tiles and the fit-max rule for P
+  if (p->kv_tile != 64 && p->kv_tile != 128) return FSATTN_E_UNSUPPORTED;
+  if (p->p_scale_rule != FSATTN_SCALE_FITMAX) return FSATTN_E_UNSUPPORTED;
   if (p->H > 65535 || p->B > 65535) return FSATTN_E_UNSUPPORTED;
   if (p->p_dump_codes) {
     if (!p->p_dump_scales || p->p_b < 0 || p->p_b >= p->B || p->p_h < 0 || p->p_h >= p->H || p->p_row0 < 0 ||
@@ -183,8 +195,16 @@ static int forward_impl(const fsattn_params* p, const fsattn_mask* mask, bool ef
   a.causal = mask ? mask->causal : 0;
   a.q_lens = mask ? mask->q_lens : nullptr;
   a.kv_lens = mask ? mask->kv_lens : nullptr;
-  // EFQ-style P: slope a = fl32(1 / fl32(128 h)) and 128 tau (exact)
-  a.efq_a = efq ? 1.0f / (128.0f * efq_h) : 0.0f;
+  // EFQ-style P: slope a = 1 / (128 h) rounded up to binary32 (so that a
+  // score exactly on a threshold gets its code), and 128 tau (exact)
+  if (efq) {
+    const double A = 1.0 / (128.0 * (double)efq_h);
+    float a32 = (float)A;
+    if ((double)a32 < A) a32 = nextafterf(a32, INFINITY);
+    a.efq_a = a32;
+  } else {
+    a.efq_a = 0.0f;
+  }
   a.efq_t128 = efq ? 128.0f * efq_tau : 0.0f;
   hipError_t e = fsattn::launch_fsattn_fwd(a, p->B, p->D, q->elem, v->elem, p->p_elem,
                                            static_cast<hipStream_t>(stream));
@@ -251,12 +271,19 @@ int fsattn_forward_bf16_baseline_masked(const void* q, const void* k, const void
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
 }
 
-int fsattn_probe_mfma(int fmt, int64_t iters, int workgroups, unsigned long long* stamps, void* stream) {
+int fsattn_probe_mfma(int fmt, int64_t iters, int workgroups, unsigned long long* stamps, int* wall_clock_khz,
+                      void* stream) {
   if (fmt != FSATTN_E4M3 && fmt != FSATTN_E2M3 && fmt != FSATTN_E2M1 && fmt != FSATTN_PROBE_BF16)
     return FSATTN_E_INVALID_ARG;
   if (iters < 1 || iters > ((int64_t)1 << 32) || workgroups < 1 || workgroups > (1 << 20) || !stamps)
     return FSATTN_E_INVALID_ARG;
   if (!aligned(stamps, 8)) return FSATTN_E_ALIGNMENT;
+  if (wall_clock_khz) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(wall_clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      return FSATTN_E_HIP;
+  }
   hipError_t e = fsattn::launch_mfma_probe(fmt, iters, workgroups, stamps, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
 }

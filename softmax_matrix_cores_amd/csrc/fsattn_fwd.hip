@@ -129,10 +129,11 @@ template <int PE> __device__ __forceinline__ constexpr int row_key(int kg, int r
 
 // Smallest BF16 pattern of a P block max for which BF16 subnormals of the
 // block convert to +0 anyway (x/X at most half the format's smallest
-// subnormal): exponent field >= 7 (E2M3), 19 (E4M3).
+// subnormal): exponent field >= 7 (E2M3), 10 (E3M2), 19 (E4M3).
 template <int PELEM> struct PFlush;
 template <> struct PFlush<E2M3> { static constexpr float t = 896.0f; };
 template <> struct PFlush<E4M3> { static constexpr float t = 2432.0f; };
+template <> struct PFlush<E3M2> { static constexpr float t = 1280.0f; };
 
 __device__ __forceinline__ float wshfl(float v, int src) { return __shfl(v, src, 64); }
 
@@ -348,11 +349,16 @@ __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, floa
 // and no BF16 stage.  A lane's 32 scores are one block (element e = 16 kg + k):
 //   E    = floor(fl32(max - T0) / 128), clamped to [-1000, 1000]
 //   E8M0 = clamp(E + 125, 0, 254)                (E2M1's top binade is 2^2)
-//   b    = -fl32(fl32(fl32(T0 + 128 E) + 128 tau) a),  a = fl32(1 / (128 h))
-//   code = clamp(floor(fma(t, a, b)), 0, 7)      (thresholds tau + j h on the
-//                                                 residual (t - T0)/128 - E)
+//   base = fl32(fl32(T0 + 128 E) + 128 tau)      (exact: integers and a dyadic)
+//   code = clamp(floor((t - base) a), 0, 7)      a = 1 / (128 h) rounded up
+// i.e. the count of thresholds tau + j h (j = 1..7) the residual
+// (t - T0)/128 - E reaches.  t - base is exact (Sterbenz near the
+// thresholds), and with the slope rounded up a score exactly on a threshold
+// lands on its integer; one a score step below stays below when that step
+// times the slope exceeds the slope's rounding times 7 plus half a step of
+// the product (so for the calibrated 128 h = 78 whenever t >= 1024).
 // Masked keys hold -inf: code 0.  FAST: the block max lies in [T0 - 16000,
-// TgEff], so E is in [-125, 127], no clamp acts and every fma result is below
+// TgEff], so E is in [-125, 127], no clamp acts and every product is below
 // (1 - tau) / h + 1 <= 4161 (h >= 1/64, tau >= -64): it fits the 16-bit
 // halves the codes are packed through.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -365,9 +371,8 @@ __device__ __forceinline__ void p_efq(const v16f (&S)[2], float m0, float m1, fl
   const int E = (int)ef;
   const uint32_t sc = FAST ? (uint32_t)(E + 125) : (uint32_t)min(max(E + 125, 0), 254);
   const float base = (T0 + (float)(128 * E)) + et128;
-  const float b = -(base * ea);
   auto ucode = [&](int e) -> float {
-    float u = __builtin_fmaf(S[e >> 4][e & 15], ea, b);
+    float u = (S[e >> 4][e & 15] - base) * ea;
     if (!FAST) u = __builtin_fminf(u, 7.0f);
     return u;
   };
@@ -377,7 +382,7 @@ __device__ __forceinline__ void p_efq(const v16f (&S)[2], float m0, float m1, fl
     // halves (8j+i, 8j+i+4) are packed first, clamped to 7 together, then
     // interleaved by nibble.  The float -> u32 converts truncate (floor for
     // u >= 0, 0 below and for -inf); the high half's convert writes straight
-    // into the upper 16 bits (SDWA), its input being an fma result
+    // into the upper 16 bits (SDWA), its input being a product
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1035,10 +1040,12 @@ hipError_t launch_d(const FwdArgs& a, int B, int D, hipStream_t s) {
 }  // namespace
 
 // supported combinations: FP8 P with FP8 V; FP6 (E2M3) P with FP6 or FP4 V;
-// EFQ-style FP4 (E2M1) P with FP6 Q/K/V or FP4 Q/K/V
+// FP6 E3M2 P with FP6 (E2M3) or FP4 Q/K/V; EFQ-style FP4 (E2M1) P with FP6
+// Q/K/V or FP4 Q/K/V
 bool fwd_supported(int qk, int ve, int pe) {
   if (pe == E4M3) return ve == E4M3 && (qk == E4M3 || qk == E2M3 || qk == E2M1);
   if (pe == E2M3) return (ve == E2M3 || ve == E2M1) && (qk == E4M3 || qk == E2M3 || qk == E2M1);
+  if (pe == E3M2) return (qk == E2M3 && ve == E2M3) || (qk == E2M1 && ve == E2M1);
   if (pe == E2M1) return (qk == E2M3 && ve == E2M3) || (qk == E2M1 && ve == E2M1);
   return false;
 }
@@ -1055,6 +1062,8 @@ hipError_t launch_fsattn_fwd(const FwdArgs& a, int B, int D, int qk, int ve, int
   FS_CASE(E2M1, E2M1, E2M3)
   FS_CASE(E2M3, E2M1, E2M3)
   FS_CASE(E4M3, E2M1, E2M3)
+  FS_CASE(E2M3, E2M3, E3M2)
+  FS_CASE(E2M1, E2M1, E3M2)
   FS_CASE(E2M3, E2M3, E2M1)
   FS_CASE(E2M1, E2M1, E2M1)
 #undef FS_CASE

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = fs.lib()
-    assert L.fsattn_abi_version() == 1
+    assert L.fsattn_abi_version() == 2
     for s in (0, -1, -2, -3, -4):
         assert L.fsattn_status_str(s)
     assert L.fsattn_status_str(-99) == b"unknown status"
@@ -45,7 +45,8 @@ def test_size_helpers(elem, bits):
 
 
 def _params(**kw):
-    base = dict(B=1, H=1, Sq=16, Skv=16, D=128, softmax_scale=128 ** -0.5, p_elem=2, tau=8.0, schraudolph_c=0.0,
+    base = dict(B=1, H=1, Sq=16, Skv=16, D=128, softmax_scale=128 ** -0.5, p_elem=2, p_scale_rule=0, tau=8.0,
+                schraudolph_c=0.0,
                 kv_tile=64, rollback_counts=None, p_dump_codes=None, p_dump_scales=None, p_b=0, p_h=0, p_row0=0,
                 p_row1=0)
     base.update(kw)
@@ -67,13 +68,20 @@ def test_forward_validation_rejects_before_launch():
     E = fs.lib()
     assert E.fsattn_forward(None, None, None, None, None, None) == -1
     assert _call(_params(D=96), _mx(), k1, v1) == -1                 # head dim
-    assert _call(_params(kv_tile=96), _mx(), k1, v1) == -1           # gate tile
+    assert _call(_params(kv_tile=80), _mx(), k1, v1) == -1           # gate tile: not a multiple of 32
+    assert _call(_params(kv_tile=0), _mx(), k1, v1) == -1
+    assert _call(_params(kv_tile=96), _mx(), k1, v1) == -2           # a multiple of 32 the kernels do not run
+    assert _call(_params(kv_tile=256), _mx(), k1, v1) == -2
+    assert _call(_params(p_scale_rule=2), _mx(), k1, v1) == -1       # rule enum
+    assert _call(_params(p_scale_rule=1), _mx(), k1, v1) == -2       # OCP-floor P: not implemented
     assert _call(_params(tau=-1.0), _mx(), k1, v1) == -1             # tau
     assert _call(_params(Skv=0), _mx(), k1, v1) == -1                # no keys
     assert _call(_params(), _mx(prescale=3.0), k1, v1) == -1         # fold prescale mismatch
     assert _call(_params(), _mx(elem=2), _mx(elem=4, prescale=1.0), v1) == -1  # Q/K formats differ
     assert _call(_params(p_elem=4), _mx(), k1, v1) == -2             # FP4 P unsupported
     assert _call(_params(p_elem=0), _mx(), k1, v1) == -2             # FP8 P needs FP8 V
+    assert _call(_params(p_elem=3, B=0), _mx(), k1, v1) == 0         # E3M2 P with E2M3 operands: accepted
+    assert _call(_params(p_elem=3), _mx(elem=0), _mx(elem=0, prescale=1.0), _mx(elem=0, prescale=1.0)) == -2
     assert _call(_params(p_dump_codes=16, p_dump_scales=16, p_row0=4, p_row1=2), _mx(), k1, v1) == -1
     assert _call(_params(), _mx(), k1, v1, out=None) == -1
     bad = fs._MxTensor(2, fs.fold_prescale(128 ** -0.5), 8, 16)      # misaligned codes
@@ -150,7 +158,7 @@ def test_bf16_masked_validation():
     assert B(16, 16, 16, 1, 1, 0, 8, 128, f, None, 16, None) == 0
 
 
-def _call_efq(p, q, k, v, tau=-3.890625, h=0.609375, out=16, mask=None):
+def _call_efq(p, q, k, v, tau=-3.875, h=0.609375, out=16, mask=None):
     return fs.lib().fsattn_forward_efq(ctypes.byref(p), mask, ctypes.c_float(tau), ctypes.c_float(h),
                                        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out, None)
 
@@ -206,3 +214,19 @@ def test_pattern_gate_tau_extreme_range_and_errors():
     assert L.fsattn_pattern_gate_tau(ctypes.c_float(-1.0), ctypes.c_float(0.0), ctypes.byref(out)) == -1
     assert L.fsattn_pattern_gate_tau(ctypes.c_float(float("nan")), ctypes.c_float(0.0), ctypes.byref(out)) == -1
     assert L.fsattn_pattern_gate_tau(ctypes.c_float(1.0), ctypes.c_float(0.0), None) == -1
+
+
+def test_fold_prescale_is_the_rounded_product():
+    """fsattn_fold_prescale(sigma) = fl32(128 log2(e) sigma) for the binary32
+    sigma it takes: the binary64 product rounded once (numpy's float32
+    rounding of the same product)."""
+    import math
+    import numpy as np
+    for sigma in (128 ** -0.5, 0.125, 1.0, 1e-3, 0.3):
+        s32 = float(np.float32(sigma))
+        want = float(np.float32(128.0 * math.log2(math.e) * s32))
+        assert fs.fold_prescale(sigma) == want
+    assert abs(fs.fold_prescale(128 ** -0.5) - 16.322231) < 1e-5
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(ValueError):
+            fs.fold_prescale(bad)
