@@ -7,8 +7,11 @@ Cases: FP6 and FP4 Q/K/V, D = 64 and 128, ragged key counts, both gate
 tiles, planted rollbacks (gate tau 0 and 1), the calibrated and other
 (tau, h) pairs, masks, and the full video shape on sampled rows.  Criteria
 as for the two-stage path: relative Frobenius error <= 1e-2, rollback counts
-equal per row, P-code mismatch <= 1e-3 (FP6/FP4 scores are exact on the
-matrix core, so the codes are expected to match exactly)."""
+equal per row, P-code mismatch <= 1e-3.  The FP6/FP4 scores are exact on
+the matrix core; the oracle compares each score with the thresholds
+tau + j h exactly, while the kernel takes one binary32 fused multiply-add per
+score whose slope 1 / (128 h) is rounded, so codes may differ for scores
+within about 2^-16 of a threshold (a few in 10^5 on these cases)."""
 import numpy as np
 import pytest
 
@@ -42,7 +45,6 @@ def test_efq_parity(oracle, case):
     w = W.custom(base, name=name, p_elem="e2m1", **kw)
     res = run_case(oracle, w, **rk)
     assert_ok(res)
-    assert res["p_mismatch"] == 0.0, res
     if w.tau < 8.0:
         assert res["total_counts"] > 0, res
     if rk.get("q_lens") is not None:
@@ -51,10 +53,11 @@ def test_efq_parity(oracle, case):
 
 def test_efq_video_sampled(oracle):
     """Full video size (B=1, H=40, S=75600, D=128) with E2M1 Q/K/V and E2M1 P,
-    in the benchmark's launch configuration; oracle rows sampled across heads,
-    with a P dump of the last rows of the last head."""
+    in the benchmark's launch configuration; 512 oracle rows sampled across
+    heads, and P dumps of the first rows, middle rows of a middle head and the
+    last rows of the last head."""
     w = W.custom("video-mxfp4", name="video-efq", p_elem="e2m1")
-    rows = W.sample_rows(w, 128).numpy()
-    res = run_case(oracle, w, rows=rows, dump_head=(0, w.H - 1), dump_rows=(w.Sq - 8, w.Sq), check_quant=False)
+    rows = W.sample_rows(w, 512).numpy()
+    res = run_case(oracle, w, rows=rows, dump_head=(0, w.H - 1), dump_rows=(w.Sq - 16, w.Sq), check_quant=False,
+                   more_dumps=[(0, 0, 0, 16), (0, w.H // 2, w.Sq // 2, w.Sq // 2 + 16)])
     assert_ok(res)
-    assert res["p_mismatch"] == 0.0, res

@@ -4,9 +4,9 @@ Small cases span several 128-key tiles, ragged query and key tails, both
 head dimensions, every supported format combination, the rollback path
 (stress rows, tau = 0) and the no-rollback limit (tau huge); P codes are
 compared for a window of rows through the library's P dump.  The benchmark
-workloads follow at their full sizes: all rows for the two small ones, a
-seeded row sample (first and last row included) for the large ones, and the
-quantizer bytes on the full tensors.
+workloads follow at their full sizes: all rows for the two small ones, 1024
+seeded rows (first and last row included) and four P-dump windows for the
+large ones, and the quantizer bytes on the full tensors.
 """
 import pytest
 import torch
@@ -45,7 +45,8 @@ def test_small_cases(oracle, name, base, kw, kv_tile):
 # has its own tests), alternating the head dimension
 COMBOS = [("e4m3", "e4m3", "e4m3"), ("e2m3", "e4m3", "e4m3"), ("e2m1", "e4m3", "e4m3"),
           ("e2m3", "e2m3", "e2m3"), ("e2m1", "e2m3", "e2m3"), ("e4m3", "e2m3", "e2m3"),
-          ("e2m1", "e2m1", "e2m3"), ("e2m3", "e2m1", "e2m3"), ("e4m3", "e2m1", "e2m3")]
+          ("e2m1", "e2m1", "e2m3"), ("e2m3", "e2m1", "e2m3"), ("e4m3", "e2m1", "e2m3"),
+          ("e2m3", "e2m3", "e3m2"), ("e2m1", "e2m1", "e3m2")]
 
 
 @pytest.mark.parametrize("i", range(len(COMBOS)), ids=["-".join(c) for c in COMBOS])
@@ -88,10 +89,31 @@ def test_stress_mxfp8_full(oracle):
     check_p(res)
 
 
+# the Schraudolph shift c != 0 (60801/8192, the RMS-optimal shift in BF16
+# pattern units) moves T0, the gate threshold and every stage-1 pattern
+@pytest.mark.parametrize("elems", [("e2m3", "e2m3", "e2m3"), ("e2m1", "e2m1", "e2m3"), ("e4m3", "e4m3", "e4m3")])
+@pytest.mark.parametrize("kv_tile", [64, 128])
+def test_schraudolph_shift(oracle, elems, kv_tile):
+    qk, ve, pe = elems
+    w = W.custom("stress-mxfp8", name=f"shift-{qk}", B=1, H=2, Sq=160, Skv=450, D=128, seed=61, qk_elem=qk,
+                 v_elem=ve, p_elem=pe)
+    res = run_case(oracle, w, dump_head=(0, 1), dump_rows=(0, 48), kv_tile=kv_tile, c=60801 / 8192)
+    assert_ok(res, defer_p=True)
+    assert res["total_counts"] > 0, res
+    check_p(res)
+
+
 @pytest.mark.parametrize("name", ["qknorm-mxfp6", "qknorm-mxfp4", "video-mxfp6", "video-mxfp4", "video-mxfp8"])
 def test_large_sampled(oracle, name):
+    """1024 seeded query rows (first and last included) against the oracle at
+    the full size; P codes of four 16-row windows: the first rows, two heads
+    in the middle and the ragged last rows of the last head."""
     w = W.WORKLOADS[name]
-    rows = W.sample_rows(w, 256 if "mxfp8" not in name else 96).numpy()
-    res = run_case(oracle, w, rows=rows, dump_head=(w.B - 1, w.H - 1), dump_rows=(w.Sq - 8, w.Sq))
+    rows = W.sample_rows(w, 1024).numpy()
+    mid = w.Sq // 2 - 8
+    more = [(0, w.H // 3, mid, mid + 16), (w.B - 1, (2 * w.H) // 3, mid + 4000 % w.Sq // 2, mid + 4000 % w.Sq // 2 + 16),
+            (w.B - 1, w.H - 1, w.Sq - 16, w.Sq)]
+    res = run_case(oracle, w, rows=rows, dump_head=(0, 0), dump_rows=(0, 16), more_dumps=more)
+    assert res["p_rows"] == 64
     assert_ok(res, defer_p=True)
     check_p(res)
