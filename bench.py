@@ -7,12 +7,16 @@ Inputs are resident in HBM before timing starts.  Reported:
 
   value        attention TFLOPS of the whole step, 4*B*H*S^2*D / step time
   roofline     the fused-forward kernel against the MX matrix-core peak
-               (algorithmic flops 4*B*H*S^2*D per launch / mean launch time,
-               HIP events on the launch stream)
+               (algorithmic flops 4*B*H*S^2*D per launch / median launch time,
+               HIP events on the launch stream; the slowest launch beside it),
+               and against the rate a pure matrix-product kernel reaches on
+               the same box (mfma_probe, with the clock it runs at)
+  sclk         the graphics clock sampled with amd-smi during the timed loop
   formats      kernel TFLOPS, MX-MFMA utilisation and speedup over the
                in-library BF16 attention kernel for each format of the workload
   cpu_baseline the CPU oracle on a bounded sample of query rows of the same
-               workload, in the same unit
+               workload, in the same unit, with the CPU model and a labelled
+               extrapolation to the whole workload
   causal       (video workloads) the fused kernel under a causal mask on the
                same inputs: 4*B*H*D*S(S+1)/2 flops (visible pairs only)
   prologue     (video workloads) the producer step fused into the quantizer:
@@ -30,9 +34,12 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
+import platform
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -75,8 +82,81 @@ def _traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+class ClockSampler:
+    """Samples the graphics clock (MHz, every XCD) with amd-smi while the timed
+    loop runs; the chip lowers its clock under sustained matrix-core load."""
+
+    def __init__(self, period_s: float = 0.25):
+        self.period, self.vals, self._stop = period_s, [], threading.Event()
+        self.th = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                d = json.loads(r.stdout)
+                g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                for key, val in g["clock"].items():
+                    if key.startswith("gfx_") and isinstance(val, dict) and isinstance(val.get("clk"), dict):
+                        v = val["clk"].get("value")
+                        if isinstance(v, (int, float)) and v > 500:  # busy XCDs only
+                            self.vals.append(float(v))
+            except Exception:  # no amd-smi or an unexpected format: no samples
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self.th.join(timeout=15)
+
+    def summary(self):
+        if not self.vals:
+            return None
+        return {"median_mhz": statistics.median(self.vals), "min_mhz": min(self.vals), "max_mhz": max(self.vals),
+                "samples": len(self.vals), "source": "amd-smi metric -c (gfx clock of each XCD, busy only)"}
+
+
+def mfma_probe(fs, fmt: str, target_ms: float = 20.0):
+    """Pure matrix-product rate of the fused kernel's instruction on this machine
+    (fsattn_probe_mfma, one workgroup of eight waves per CU): TFLOP/s and the
+    shader clock it ran at (s_memtime against the constant-rate counter)."""
+    import torch
+
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    per_round = {"e2m3": 32, "e2m1": 32, "e4m3": 64, "bf16": 128}[fmt] * 8  # cycles per round per SIMD at peak
+    iters = max(100, int(target_ms * 1e-3 * 2.0e9 / per_round))
+    fs.probe_mfma(fmt, 100, wgs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    st, khz = fs.probe_mfma(fmt, iters, wgs)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    s = st.cpu().double()
+    ratio = float(((s[:, 1] - s[:, 0]) / (s[:, 3] - s[:, 2])).median())
+    return {"fmt": fmt, "tflops": round(wgs * 8 * iters * 4 * 2 * 32 * 32 * 64 / ms / 1e9, 1),
+            "clock_mhz": round(ratio * khz / 1e3, 1) if khz > 0 else None, "ms": round(ms, 3), "workgroups": wgs}
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def time_path(fs, W, w, q, k, v, steps, warmup):
-    """Time `steps` whole-path steps; returns (ms_per_step, fwd_ms_mean, quant_ms_mean, out, counts)."""
+    """Time `steps` whole-path steps; returns (ms_per_step, fwd_ms_median, fwd_ms_slowest, fwd_ms_mean,
+    quant_ms_median, out, counts)."""
     import torch
 
     dev = q.device
@@ -115,11 +195,11 @@ def time_path(fs, W, w, q, k, v, steps, warmup):
     total = t0.elapsed_time(t1)
     fwd = [e[1].elapsed_time(e[2]) for e in evs]
     qnt = [e[0].elapsed_time(e[1]) for e in evs]
-    return total / steps, sum(fwd) / len(fwd), max(fwd), sum(qnt) / len(qnt), out, counts
+    return total / steps, statistics.median(fwd), max(fwd), statistics.mean(fwd), statistics.median(qnt), out, counts
 
 
 def time_fused_causal(fs, w, q, k, v, steps, warmup):
-    """Mean fused-kernel time (ms) under a causal mask, HIP events on the launch stream."""
+    """Median fused-kernel time (ms) under a causal mask, HIP events on the launch stream."""
     import torch
 
     st = torch.cuda.current_stream()
@@ -143,7 +223,7 @@ def time_fused_causal(fs, w, q, k, v, steps, warmup):
         b.record(st)
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) for a, b in ev]
-    return sum(ts) / len(ts), int(counts.sum().item())
+    return statistics.median(ts), int(counts.sum().item())
 
 
 def time_prologue(fs, w, q, k, steps):
@@ -200,7 +280,7 @@ def time_bf16(fs, w, q, k, v, steps, warmup, causal=False):
         b.record(st)
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) for a, b in ev]
-    return sum(ts) / len(ts), out
+    return statistics.median(ts), out
 
 
 def cpu_baseline(w, q, k, v, budget_s: float = 15.0):
@@ -245,9 +325,13 @@ def cpu_baseline(w, q, k, v, budget_s: float = 15.0):
         O.forward(p, Qo, Ko, Vo, rows=rows)
         dt = time.perf_counter() - t
     flops = 4.0 * n * w.Skv * w.D
+    total_rows = w.B * w.H * w.Sq
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
             "sample": f"{n} query rows of head 0 of {w.name} (all {w.Skv} keys), fused forward only; "
-                      f"{dt:.1f} s wall, {flops / n:.3g} flop/row"}
+                      f"{dt:.1f} s wall, {flops / n:.3g} flop/row",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "rows_per_s": round(n / dt, 1),
+            "extrapolated_full_workload_s": round(dt / n * total_rows, 1),
+            "extrapolated_note": f"measured time per row x {total_rows} rows (B*H*S), not a measured run"}
 
 
 def main():
@@ -305,13 +389,17 @@ def main():
 
     formats = {}
     main_res = None
+    clocks = None
     for vw in variants:
         print(f"[bench] fused {vw.name}", file=sys.stderr, flush=True)
-        st_ms, fwd_ms, fwd_max, q_ms, out, counts = time_path(fs, W, vw, q, k, v, args.steps if vw is w else
-                                                              max(3, args.steps // 2), args.warmup)
+        with ClockSampler() as cs:
+            st_ms, fwd_ms, fwd_max, fwd_mean, q_ms, out, counts = time_path(fs, W, vw, q, k, v, args.steps if vw is w else
+                                                                  max(3, args.steps // 2), args.warmup)
+        if vw is w:
+            clocks = cs.summary()
         k_tflops = vw.flops / (fwd_ms * 1e-3) / 1e12
         rec = {"kernel_tflops": round(k_tflops, 2), "kernel_ms": round(fwd_ms, 4), "kernel_ms_slowest": round(fwd_max, 4),
-               "quantize_ms": round(q_ms, 4), "step_ms": round(st_ms, 4),
+               "kernel_ms_mean": round(fwd_mean, 4), "quantize_ms": round(q_ms, 4), "step_ms": round(st_ms, 4),
                "mx_mfma_util": round(k_tflops / _peak_for(vw), 4),
                "rollbacks": int(counts.sum().item())}
         if bf16_ms is not None:
@@ -353,6 +441,16 @@ def main():
             sched["speedup_vs_bf16_incl_quant"] = round(bf16_ms / sched["step_ms"], 3)
         formats["video-schedule-6xmxfp6-14xmxfp4"] = sched
 
+    # the matrix cores' measured rate on this machine, per format, at the clock
+    # they hold under a pure product load
+    print("[bench] matrix-core probe", file=sys.stderr, flush=True)
+    probes = {f: mfma_probe(fs, f) for f in ("e2m3", "e2m1", "e4m3", "bf16")}
+    for name, rec in formats.items():
+        vw = W.WORKLOADS.get(name)
+        if vw is not None and "kernel_tflops" in rec:
+            slow = min((vw.qk_elem, vw.v_elem, vw.p_elem), key=lambda f: probes[f if f in probes else "e2m1"]["tflops"])
+            rec["util_vs_measured_peak"] = round(rec["kernel_tflops"] / probes[slow]["tflops"], 4)
+
     st_ms, fwd_ms, rec = main_res
     value = w.flops / (st_ms * 1e-3) / 1e12
     achieved = w.flops / (fwd_ms * 1e-3) / 1e12
@@ -366,15 +464,23 @@ def main():
                    "p": w.p_elem, "tau": w.tau, "kv_tile": w.kv_tile},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": _traffic(w.name),
-                     "kernel": "fsattn_fwd_kernel", "flops_per_launch": w.flops},
+                     "kernel": "fsattn_fwd_kernel", "flops_per_launch": w.flops,
+                     "timing": "median of the timed launches (HIP events on the launch stream)",
+                     "kernel_ms_median": rec["kernel_ms"], "kernel_ms_mean": rec["kernel_ms_mean"],
+                     "kernel_ms_slowest": rec["kernel_ms_slowest"],
+                     "measured_peak": probes[w.qk_elem if w.qk_elem in probes else "e2m1"]["tflops"],
+                     "frac_of_measured_peak": rec.get("util_vs_measured_peak")},
+        "sclk": clocks,
+        "mfma_probe": probes,
         "formats": formats,
     }
     if line_prologue is not None:
         line["prologue"] = line_prologue
     if bf16_ms is not None:
-        line["bf16_baseline"] = {"kernel_ms": round(bf16_ms, 4),
-                                 "tflops": round(w.flops / (bf16_ms * 1e-3) / 1e12, 2),
-                                 "bf16_mfma_util": round(w.flops / (bf16_ms * 1e-3) / 1e12 / PEAK["bf16"], 4)}
+        bt = w.flops / (bf16_ms * 1e-3) / 1e12
+        line["bf16_baseline"] = {"kernel_ms": round(bf16_ms, 4), "tflops": round(bt, 2),
+                                 "bf16_mfma_util": round(bt / PEAK["bf16"], 4),
+                                 "util_vs_measured_peak": round(bt / probes["bf16"]["tflops"], 4)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
