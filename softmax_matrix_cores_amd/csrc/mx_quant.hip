@@ -19,31 +19,6 @@ namespace fsattn {
 // bf16 bit pattern -> fp32 (exact)
 __device__ __forceinline__ float bf16_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
 
-// Round-to-nearest-even of y (already divided by the block scale) into a
-// 6-bit format (E2M3 or E3M2), saturating at the largest value, sign kept.
-// The quantum of y's binade is a power of two, so y * 2^-quantum is exact and
-// v_rndne_f32 performs the one rounding.
-template <int ELEM>
-__device__ __forceinline__ uint32_t sw_encode6(float y) {
-  constexpr int MB = (ELEM == E2M3) ? 3 : 2;          // mantissa bits
-  constexpr int BIAS = (ELEM == E2M3) ? 1 : 3;
-  constexpr int EMIN = 1 - BIAS;                      // exponent of the smallest normal
-  const uint32_t sign = __float_as_uint(y) >> 31;
-  float a = fminf(fabsf(y), Fmt<ELEM>::maxnorm);
-  int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;
-  e = max(e, EMIN);
-  const float scale = __uint_as_float((uint32_t)(MB - e + 127) << 23);  // 2^(MB - e)
-  uint32_t n = (uint32_t)__builtin_rintf(a * scale);                    // 0 .. 2^(MB+1)
-  uint32_t mag;
-  if (e == EMIN && n < (1u << MB)) {
-    mag = n;  // subnormal
-  } else {
-    if (n == (2u << MB)) { e += 1; n = 1u << MB; }
-    mag = ((uint32_t)(e + BIAS) << MB) | (n - (1u << MB));
-  }
-  return (sign << 5) | mag;
-}
-
 // Convert 32 fp32 values into packed element codes of block scale X (the
 // hardware converters divide by X).  w receives bits dwords.  bf16_exact:
 // every value is an exact bf16 (no prescale applied).
@@ -63,29 +38,26 @@ __device__ __forceinline__ void encode32(const float* x, float X, uint32_t* w, b
       w[i] = (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
     }
   } else if constexpr (ELEM == E2M3 || ELEM == E3M2) {
-    if (bf16_exact) {
-      // the values are exact bf16 (no prescale): hardware bf16 -> FP6 converter
-      v32bf v;
+    // hardware bf16 -> FP6 converter (RNE of v / X).  Values that are not
+    // exact bf16 (a prescale was applied) are first rounded to odd into bf16:
+    // truncated, with the OR of the dropped bits kept in the last bit.  bf16
+    // keeps at least two more bits than either 6-bit format at every
+    // magnitude (subnormals included), so the converter's rounding of the
+    // rounded-to-odd value is the correctly rounded result of the fp32 value
+    // (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
+    // proved algorithms using rounding to odd", IEEE Trans. Computers 2008).
+    v32bf v;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(x[i]) >> 16));
-      v6i r;
-      if constexpr (ELEM == E2M3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, X);
-      else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(v, X);
-#pragma unroll
-      for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
-    } else {
-      // fp32 values: exact software round-to-nearest-even into the 6-bit grid
-      const float inv = 1.0f / X;  // exact: X is a power of two (2^-127 .. 2^127)
-#pragma unroll
-      for (int i = 0; i < 6; ++i) w[i] = 0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        uint32_t c = sw_encode6<ELEM>(x[j] * inv);
-        const int pos = 6 * j;
-        w[pos >> 5] |= c << (pos & 31);
-        if ((pos & 31) > 26) w[(pos >> 5) + 1] |= c >> (32 - (pos & 31));
-      }
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t u = __float_as_uint(x[i]);
+      const uint32_t b = bf16_exact ? (u >> 16) : ((u >> 16) | min(u & 0xFFFFu, 1u));
+      v[i] = __builtin_bit_cast(__bf16, (uint16_t)b);
     }
+    v6i r;
+    if constexpr (ELEM == E2M3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, X);
+    else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(v, X);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
   } else {  // E2M1
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -281,56 +253,52 @@ __global__ void __launch_bounds__(256) mxq_axis1_kernel(const uint16_t* __restri
   scales[((m * nb + kb) * 32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)code;
 }
 
-// axis 1, tiled (cols 64 or 128, 16-byte rows): a workgroup quantizes keys
-// [128 t, 128 t + 128) of every column of matrix m.  The bf16 tile (32 KiB at
-// most, so four workgroups share a CU's LDS) comes in with 16-byte coalesced
-// loads; in LDS each 16-byte chunk of row r sits rotated by 16 ((r / 32) % 4)
-// columns (mod cols), so that the column reads below (lanes = 4 key blocks x
-// 16 columns) hit 32 distinct banks.  Each thread
-// then quantizes (column, 32-key block) units with the key block fastest, so
-// neighbouring threads write neighbouring blocks of one column: the packed
-// codes leave as contiguous runs.  The arithmetic per block is the same as
+// axis 1, direct (cols 64 or 128, rows 16-byte aligned): lane (key block kb,
+// column octet co) loads 16 bytes (8 columns) of each of the block's 32 key
+// rows and quantizes the eight column blocks from registers.  The COLS / 8
+// lanes of one key block read whole rows (a wave covers 64 / (COLS / 8)
+// consecutive key blocks), and every lane has 32 loads in flight before it
+// converts.  Neighbouring key blocks of a column are written by neighbouring
+// lane groups, as contiguous runs.  The arithmetic per block is the same as
 // mxq_axis1_kernel's (same quant_block, zero padding past the last key).
-constexpr int AX1_KT = 128;  // keys per tile
+constexpr int AX1_TB = 256;  // threads per workgroup
 template <int ELEM, int COLS>
-__global__ void __launch_bounds__(256) mxq_axis1_tiled_kernel(const uint16_t* __restrict__ src, int64_t rows,
-                                                              int64_t ld, int64_t nb, float prescale, bool fitmax,
-                                                              uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales) {
+__global__ void __launch_bounds__(AX1_TB) mxq_axis1_direct_kernel(const uint16_t* __restrict__ src, int64_t n_mat,
+                                                                  int64_t rows, int64_t ld, int64_t nb,
+                                                                  float prescale, bool fitmax,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales) {
   constexpr int BB = Fmt<ELEM>::bits * 4;
-  constexpr int NBT = AX1_KT / 32;  // key blocks per tile
-  constexpr int CPR = COLS / 8;     // 16-byte chunks per row
-  constexpr int ROT = 64 / NBT;     // rotation step (columns) per key block
-  __shared__ __attribute__((aligned(16))) uint16_t tile[AX1_KT * COLS];
-  const int64_t m = blockIdx.y;
-  const int64_t r0 = (int64_t)blockIdx.x * AX1_KT;
-  const int rows_t = (int)min((int64_t)AX1_KT, rows - r0);  // >= 1
-  const uint16_t* base = src + (m * rows + r0) * ld;
-  for (int c = threadIdx.x; c < AX1_KT * CPR; c += 256) {
-    const int r = c / CPR, q = c - r * CPR;
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rows_t) u = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + 8 * q);
-    const int col = (8 * q + ROT * ((r >> 5) & (NBT - 1))) & (COLS - 1);
-    *reinterpret_cast<uint4*>(tile + r * COLS + col) = u;
-  }
-  __syncthreads();
-  const int nbt = (rows_t + 31) / 32;
-  for (int u = threadIdx.x; u < NBT * COLS; u += 256) {
-    const int kb = u % NBT, d = u / NBT;
-    if (kb >= nbt) continue;
-    const int col = (d + ROT * kb) & (COLS - 1);
+  constexpr int LPB = COLS / 8;   // lanes per key block
+  constexpr int KBW = 64 / LPB;   // key blocks per wave
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * AX1_TB + threadIdx.x) >> 6;
+  const int64_t wpm = (nb + KBW - 1) / KBW;  // waves per matrix
+  const int64_t m = wave / wpm;
+  const int64_t kb = (wave - m * wpm) * KBW + lane / LPB;
+  if (m >= n_mat || kb >= nb) return;
+  const int co = lane % LPB;
+  const uint16_t* p = src + (m * rows + kb * 32) * ld + 8 * co;
+  const int nrow = (int)min((int64_t)32, rows - kb * 32);
+  uint4 r[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    r[j] = j < nrow ? *reinterpret_cast<const uint4*>(p + (int64_t)j * ld) : make_uint4(0u, 0u, 0u, 0u);
+  const bool exact = prescale == 1.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
     float x[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const int r = kb * 32 + j;
-      x[j] = (r < rows_t) ? bf16_to_f32(tile[r * COLS + col]) * prescale : 0.0f;
+      const uint32_t wv = (e < 2) ? r[j].x : (e < 4) ? r[j].y : (e < 6) ? r[j].z : r[j].w;
+      const float f = bf16_to_f32((e & 1) ? (wv >> 16) : (wv & 0xFFFFu));
+      x[j] = exact ? f : f * prescale;
     }
     uint32_t w[8];
-    const uint32_t code = quant_block<ELEM>(x, fitmax, w, prescale == 1.0f);
-    const int64_t kbg = (int64_t)blockIdx.x * NBT + kb;
-    const int64_t o = (m * COLS + d) * nb + kbg;
-    store_block<BB>(codes + o * BB, w);
-    scales[((m * nb + kbg) * 32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)code;
+    const uint32_t code = quant_block<ELEM>(x, fitmax, w, exact);
+    const int d = 8 * co + e;
+    store_block<BB>(codes + ((m * COLS + d) * nb + kb) * BB, w);
+    scales[((m * nb + kb) * 32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)code;
   }
 }
 
@@ -351,16 +319,18 @@ static hipError_t launch_elem(const uint16_t* src, int64_t n_mat, int64_t rows, 
                          prescale, fitmax, codes, scales);
   } else {
     int64_t nb = (rows + 31) / 32, total = n_mat * nb * cols;
-    const bool tiled = (cols == 64 || cols == 128) && (ld % 8 == 0) &&
-                       ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && n_mat <= 65535;
-    if (tiled) {
-      dim3 grid((unsigned)((rows + AX1_KT - 1) / AX1_KT), (unsigned)n_mat);
+    const bool direct = (cols == 64 || cols == 128) && (ld % 8 == 0) &&
+                        ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
+    if (direct) {
+      const int kbw = 64 / (int)(cols / 8);
+      const int64_t waves = n_mat * ((nb + kbw - 1) / kbw);
+      dim3 grid((unsigned)((waves * 64 + AX1_TB - 1) / AX1_TB));
       if (cols == 128)
-        hipLaunchKernelGGL((mxq_axis1_tiled_kernel<ELEM, 128>), grid, dim3(TB), 0, stream, src, rows, ld, nb,
-                           prescale, fitmax, codes, scales);
+        hipLaunchKernelGGL((mxq_axis1_direct_kernel<ELEM, 128>), grid, dim3(AX1_TB), 0, stream, src, n_mat, rows,
+                           ld, nb, prescale, fitmax, codes, scales);
       else
-        hipLaunchKernelGGL((mxq_axis1_tiled_kernel<ELEM, 64>), grid, dim3(TB), 0, stream, src, rows, ld, nb,
-                           prescale, fitmax, codes, scales);
+        hipLaunchKernelGGL((mxq_axis1_direct_kernel<ELEM, 64>), grid, dim3(AX1_TB), 0, stream, src, n_mat, rows,
+                           ld, nb, prescale, fitmax, codes, scales);
     } else {
       dim3 grid((unsigned)((total + TB - 1) / TB));
       hipLaunchKernelGGL((mxq_axis1_kernel<ELEM>), grid, dim3(TB), 0, stream, src, n_mat, rows, cols, ld, nb,
