@@ -258,12 +258,12 @@ int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const
  *   E8M0 = clamp(E - 2 + 127, 0, 254)
  *   code = #{ j in 1..7 : l - E >= efq_tau + j efq_h }   (code 7 is E2M1's 6.0)
  * i.e. the residual l - E is compared with uniformly spaced thresholds.  The
- * kernel counts them as clamp(floor((t - base) a), 0, 7) with the exact
- * base = T0 + 128 E + 128 efq_tau and a = 1 / (128 efq_h) rounded up to
- * binary32.  A score exactly on a threshold gets the higher code.  For the
- * calibrated spacing (128 efq_h = 78) the count is exact for every t >= 1024
- * (binary32 step 2^-13 or coarser); for other spacings, or smaller t, a score
- * a few binary32 steps below a threshold may also get it.  Masked keys
+ * kernel counts them as clamp(floor(fma(t, a, b)), 0, 7) with
+ * a = 1 / (128 efq_h) and b = -(T0 + 128 E + 128 efq_tau) a, both rounded up
+ * to binary32: a score exactly on a threshold gets the higher code, and the
+ * count is exact except that a score exactly one binary32 step below a
+ * threshold may also get it (for the calibrated spacing 128 efq_h = 78 only
+ * when t >= 16384).  Masked keys
  * get code 0.  (efq_tau, efq_h) are calibrated offline; -3.875 and
  * 0.609375 minimize the output error on synthetic MXFP4 attention.
  *

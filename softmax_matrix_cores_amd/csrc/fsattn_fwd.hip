@@ -350,17 +350,24 @@ __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, floa
 //   E    = floor(fl32(max - T0) / 128), clamped to [-1000, 1000]
 //   E8M0 = clamp(E + 125, 0, 254)                (E2M1's top binade is 2^2)
 //   base = fl32(fl32(T0 + 128 E) + 128 tau)      (exact: integers and a dyadic)
-//   code = clamp(floor((t - base) a), 0, 7)      a = 1 / (128 h) rounded up
+//   code = clamp(floor(fma(t, a, b)), 0, 7)      a = 1 / (128 h), b = -base a,
+//                                                both rounded up
 // i.e. the count of thresholds tau + j h (j = 1..7) the residual
-// (t - T0)/128 - E reaches.  t - base is exact (Sterbenz near the
-// thresholds), and with the slope rounded up a score exactly on a threshold
-// lands on its integer; one a score step below stays below when that step
-// times the slope exceeds the slope's rounding times 7 plus half a step of
-// the product (so for the calibrated 128 h = 78 whenever t >= 1024).
+// (t - T0)/128 - E reaches.  With a and b rounded up, a score exactly on a
+// threshold (t = base + 128 j h) lands at or above j.  A score one binary32
+// step below one can land there too when that step times a is below b's
+// rounding; for the calibrated 128 h = 78 this happens only at t >= 16384,
+// for a score exactly one step below a threshold (an exact emulation over
+// every binary32 score of the fast path's range finds no other case).
 // Masked keys hold -inf: code 0.  FAST: the block max lies in [T0 - 16000,
 // TgEff], so E is in [-125, 127], no clamp acts and every product is below
 // (1 - tau) / h + 1 <= 4161 (h >= 1/64, tau >= -64): it fits the 16-bit
 // halves the codes are packed through.
+__device__ __forceinline__ float next_up(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if (x == 0.0f) return __uint_as_float(1u);
+  return __uint_as_float((int32_t)u >= 0 ? u + 1u : u - 1u);
+}
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 template <bool FAST>
 __device__ __forceinline__ void p_efq(const v16f (&S)[2], float m0, float m1, float T0, float ea, float et128,
@@ -371,8 +378,11 @@ __device__ __forceinline__ void p_efq(const v16f (&S)[2], float m0, float m1, fl
   const int E = (int)ef;
   const uint32_t sc = FAST ? (uint32_t)(E + 125) : (uint32_t)min(max(E + 125, 0), 254);
   const float base = (T0 + (float)(128 * E)) + et128;
+  // b = -base a rounded up: the product's rounding error decides the step
+  const float bn = -base * ea;
+  const float b = __builtin_fmaf(-base, ea, -bn) > 0.0f ? next_up(bn) : bn;
   auto ucode = [&](int e) -> float {
-    float u = (S[e >> 4][e & 15] - base) * ea;
+    float u = __builtin_fmaf(S[e >> 4][e & 15], ea, b);
     if (!FAST) u = __builtin_fminf(u, 7.0f);
     return u;
   };
