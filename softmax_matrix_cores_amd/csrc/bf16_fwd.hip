@@ -19,9 +19,14 @@
 //     operand of the PV product (no shuffles).
 //   * K is streamed by LDS DMA into a 4-slot ring in operand order (one
 //     lane-contiguous ds_read_b128 per operand).  V is streamed row-major
-//     into a 3-slot staging ring, and the workgroup transposes each step once
-//     (4x4 blocks of 16-bit elements in registers) into V^T operands in
-//     operand order, double buffered.  Loads run three steps ahead.
+//     into a 4-slot ring and read as the PV product's B operand with the
+//     transposing LDS read ds_read_b64_tr_b16: within each group of 16 lanes,
+//     lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+//     4e + i / 4 (e = 0..3), so 16 lanes addressing a 4-key x 16-feature
+//     block each receive the 4 keys of one feature (layout measured on
+//     gfx950).  The DMA places each row's 16-byte chunks XOR-swizzled by the
+//     row index, so that the 4 rows such a group reads fall in distinct
+//     quarters of the LDS banks.  Loads run three steps ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,31 +38,38 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf_b __attribute__((ext_vector_type(2)));
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s16 lds_v4s16;
 
 constexpr int BW = 8;         // waves per workgroup
 constexpr int BQ = 32;        // queries per wave
 constexpr int BQG = BW * BQ;  // queries per workgroup
 constexpr int BK = 64;        // keys per step
-constexpr int KR = 4;         // K ring slots
-constexpr int VR = 3;         // V staging ring slots
+constexpr int RS = 4;         // K and V ring slots
 
 template <int D> struct BGeo {
   static constexpr int NC = D / 16;          // 16-feature chunks of a score product
   static constexpr int NO = D / 32;          // 32-feature blocks of the PV product
   static constexpr int ROW = 2 * D;          // bytes of a K or V row
   static constexpr int KSLOT = 2 * NC * 1024;  // K operands of a step: 2 key groups x NC chunks
-  static constexpr int VSLOT = BK * ROW;       // V rows of a step, row-major
-  static constexpr int VT = 4 * NO * 1024;     // V^T operands: 4 key chunks x NO blocks
+  static constexpr int VSLOT = BK * ROW;       // V rows of a step, row-major, chunks swizzled
   static constexpr int K_OFF = 0;
-  static constexpr int VS_OFF = K_OFF + KR * KSLOT;
-  static constexpr int VT_OFF = VS_OFF + VR * VSLOT;
-  static constexpr int LDS = VT_OFF + 2 * VT;
+  static constexpr int V_OFF = K_OFF + RS * KSLOT;
+  static constexpr int LDS = V_OFF + RS * VSLOT;
   // DMA per step: one 16-byte load per K operand region (2 NC), VSLOT/1024
   // loads of V rows; waves 0-3 load K, waves 4-7 V, the same count each
   static constexpr int NLOAD = 2 * NC;
   static constexpr int PER_WAVE = NLOAD / 4;
   static_assert(VSLOT / 1024 == NLOAD, "K and V sides issue the same number of loads");
 };
+
+// 16-byte chunk c of V row r sits at chunk c ^ vswz(r) of its LDS row: the
+// 4 consecutive rows a transposing read covers then use the four 64-byte
+// quarters of the 256-byte bank cycle (row r's quarter is (c / 4) ^ (r % 4)
+// for D = 128, 2 (r % 2) + ((c / 4) ^ ((r / 2) % 2)) for D = 64)
+template <int D> __device__ __forceinline__ constexpr int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 // key (0..31 of a key group) fed to row r of the K operand: accumulator row
 // 8i + 4h + j then holds key 16(i/2) + 8h + 4(i%2) + j
@@ -130,9 +142,12 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
       lofs[j] = __builtin_amdgcn_readfirstlane(G::K_OFF + L * 1024);
       vofs[j] = (32 * kg + brow_key(n)) * G::ROW + 32 * c + 16 * hh;
     } else {
-      // V rows: load L covers 1024 bytes of the row-major step
-      lofs[j] = __builtin_amdgcn_readfirstlane(G::VS_OFF + L * 1024);
-      vofs[j] = L * 1024 + 16 * lane;
+      // V rows: load L fills 1024 bytes of the row-major step; LDS chunk c of
+      // row r receives global chunk c ^ vswz(r)
+      constexpr int CPR = G::ROW / 16;  // chunks per row
+      const int r = (L * 1024 + 16 * lane) / G::ROW, c = lane % CPR;
+      lofs[j] = __builtin_amdgcn_readfirstlane(G::V_OFF + L * 1024);
+      vofs[j] = r * G::ROW + 16 * (c ^ vswz<D>(r));
     }
   }
   const uint64_t base = (uint64_t)(uintptr_t)((kside ? k : v) + (size_t)bh * Skv * D);
@@ -149,45 +164,34 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
   };
   const uint32_t lds0 = lds_addr(smem);
   int snext = 0;  // next step to fetch
-  int kfill = 0, vfill = 0;  // its K and V ring slots
   auto issue = [&]() {
-    const uint32_t slot = lds0 + (uint32_t)(kside ? kfill * G::KSLOT : vfill * G::VSLOT);
+    const int fill = snext & (RS - 1);
+    const uint32_t slot = lds0 + (uint32_t)(kside ? fill * G::KSLOT : fill * G::VSLOT);
     const uint32_t keep = m0_save();
 #pragma unroll
     for (int j = 0; j < G::PER_WAVE; ++j) dma_x4(rc, slot, (uint32_t)lofs[j], vofs[j]);
     m0_restore(keep);
     advance();
     ++snext;
-    kfill = kfill == KR - 1 ? 0 : kfill + 1;
-    vfill = vfill == VR - 1 ? 0 : vfill + 1;
   };
 
-  // ---- transpose of one step's V rows (staging slot vs) into V^T operands
-  // (buffer vt): thread item (key quad kq, feature quad dq)
-  auto transpose = [&](int vs, int vt) {
-    const uint8_t* st = smem + G::VS_OFF + vs * G::VSLOT;
-    uint8_t* dst = smem + G::VT_OFF + vt * G::VT;
-    constexpr int ITEMS = 16 * (D / 4);
+  // ---- PV B operand (V, 8 keys of 16-key chunk t for feature 32 o + n, n =
+  // lane % 32, keys 8h .. 8h + 7): two transposing reads of 4 keys each.
+  // Supplying lane j of a 16-lane group addresses row (key) kq + j / 4,
+  // features 16 (group % 2) + 4 (j % 4) .. + 3 of block o.
+  const int grp = lane >> 4, jl = lane & 15;
+  const int vrow0 = 8 * (grp >> 1) + (jl >> 2);                    // + 16 t + 4 half
+  const int vcol = 2 * (16 * (grp & 1) + 4 * (jl & 3));             // bytes within the block's 64
+  auto v_op = [&](uint32_t vslot, int t, int o) -> v8bf {
+    v4s16 r2[2];
 #pragma unroll
-    for (int it = tid; it < ITEMS; it += BW * 64) {
-      const int kq = it / (D / 4), dq = it % (D / 4);
-      uint2 r[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = *reinterpret_cast<const uint2*>(st + (4 * kq + e) * G::ROW + 8 * dq);
-      // key k = 4 kq + e, feature d = 4 dq + f: chunk t = kq / 4, lane half
-      // (kq % 4) / 2, element 4 (kq % 2) + e of lane (h, d % 32)
-      const int t = kq >> 2, h2 = (kq >> 1) & 1;
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int d = 4 * dq + f;
-        const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of (b, a)
-        const uint32_t w0 = (f < 2) ? r[0].x : r[0].y, w1 = (f < 2) ? r[1].x : r[1].y;
-        const uint32_t w2 = (f < 2) ? r[2].x : r[2].y, w3 = (f < 2) ? r[3].x : r[3].y;
-        const uint2 o2 = make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
-        const int region = t * NO + (d >> 5);
-        *reinterpret_cast<uint2*>(dst + region * 1024 + (32 * h2 + (d & 31)) * 16 + 8 * (kq & 1)) = o2;
-      }
+    for (int half = 0; half < 2; ++half) {
+      const int row = 16 * t + 4 * half + vrow0;
+      const int byte = 64 * o + vcol;  // chunk byte / 16, 8-byte half (byte / 8) % 2
+      const uint32_t off = (uint32_t)(row * G::ROW + 16 * ((byte >> 4) ^ vswz<D>(row)) + (byte & 15));
+      r2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(size_t)(vslot + off));
     }
+    return __builtin_bit_cast(v8bf, __builtin_shufflevector(r2[0], r2[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
   // ---- Q^T operands (B of S^T): lane (q, h), chunk c: Q[q][16c + 8h .. +8]
@@ -207,24 +211,20 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
   float m = -INFINITY;  // running max of query n (scaled, log2 units), lanes n and n + 32 agree
   float lsum = 0.0f;    // this lane's share of the row sum
 
-  // prologue: steps 0..2 in flight; step 0 transposed before the loop
+  // prologue: steps 0..2 in flight
   for (int s = 0; s < 3; ++s) issue();
-  wait_vm<2 * G::PER_WAVE>();
-  barrier();
-  transpose(0, 0);
-  int kread = 0, vstage = 1;  // K ring slot of step u; staging slot of step u + 1
 
   for (int u = 0; u < ns; ++u) {
-    // steps <= u + 1 landed; after the barrier the loads of step u + 3 reuse
-    // the K slot of step u - 1 and the staging slot of step u, both consumed
-    wait_vm<G::PER_WAVE>();
-    wait_lgkm0();  // the previous step's transpose writes (ds_write) are done
+    // steps <= u landed (u + 1 and u + 2 may be in flight); after the barrier
+    // the loads of step u + 3 reuse the slots of step u - 1, which every wave
+    // finished reading before it
+    wait_vm<2 * G::PER_WAVE>();
     barrier();
     issue();
-    transpose(vstage, (u + 1) & 1);
+    const int slot = u & (RS - 1);
 
     // ---- S^T = K Q^T for the step's two key groups
-    const uint8_t* ks = smem + G::K_OFF + kread * G::KSLOT;
+    const uint8_t* ks = smem + G::K_OFF + slot * G::KSLOT;
     v16f S[2];
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
@@ -253,11 +253,12 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
           if (key >= nk) S[kg][e] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // row maximum with IEEE 754-2019 maximum (v_maximum3_f32): unlike fmaxf
+    // it needs no quieting of its inputs, and scores are finite or -inf
+    float mx = __builtin_elementwise_maximum(S[0][0], S[0][1]);
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kg][e]);
+    for (int i = 2; i < 32; i += 2)
+      mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, S[i >> 4][i & 15]), S[i >> 4][(i + 1) & 15]);
     mx *= c_log2;
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = __builtin_fmaxf(m, mx);
@@ -280,29 +281,30 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
     // p = exp2(s c - m), l += p, P operands of the four 16-key chunks (a row
     // that has seen no key yet keeps m = -inf: its masked scores give p = 0)
     const float mref = m > -INFINITY ? m : 0.0f;
+    // l sums the bf16 p that the PV product uses, two at a time (v_dot2 with
+    // ones), in four independent chains
     uint32_t pw[16];
+    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kg][e], c_log2, -mref));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kg][e + 1], c_log2, -mref));
-        lsum += p0 + p1;
-        pw[8 * kg + e / 2] = pk_bf16(p0, p1);
+        const int i = 8 * kg + e / 2;
+        pw[i] = pk_bf16(p0, p1);
+        lp[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf_b, pw[i]),
+                                                    __builtin_bit_cast(v2bf_b, 0x3F803F80u), lp[i & 3], false);
       }
+    lsum += (lp[0] + lp[1]) + (lp[2] + lp[3]);
     // ---- O += P V: chunk t = 2 kg + (i / 2) holds registers 8t .. 8t + 7
-    const uint8_t* vt = smem + G::VT_OFF + (u & 1) * G::VT;
+    const uint32_t vslot = lds0 + (uint32_t)(G::V_OFF + slot * G::VSLOT);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const v8bf pa = __builtin_bit_cast(v8bf, uint4{pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]});
 #pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        const v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(vt + (t * NO + o) * 1024 + 16 * lane));
-        O[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, b, O[o], 0, 0, 0);
-      }
+      for (int o = 0; o < NO; ++o) O[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, v_op(vslot, t, o), O[o], 0, 0, 0);
     }
-    kread = kread == KR - 1 ? 0 : kread + 1;
-    vstage = vstage == VR - 1 ? 0 : vstage + 1;
   }
   wait_vm<0>();  // loads past the end are still in flight
 
