@@ -86,8 +86,8 @@ class ClockSampler:
     """Samples the graphics clock (MHz, every XCD) with amd-smi while the timed
     loop runs; the chip lowers its clock under sustained matrix-core load."""
 
-    def __init__(self, period_s: float = 0.25):
-        self.period, self.vals, self._stop = period_s, [], threading.Event()
+    def __init__(self, period_s: float = 0.25, enabled: bool = True):
+        self.period, self.vals, self._stop, self.enabled = period_s, [], threading.Event(), enabled
         self.th = threading.Thread(target=self._run, daemon=True)
 
     def _run(self):
@@ -107,12 +107,14 @@ class ClockSampler:
             self._stop.wait(self.period)
 
     def __enter__(self):
-        self.th.start()
+        if self.enabled:
+            self.th.start()
         return self
 
     def __exit__(self, *exc):
         self._stop.set()
-        self.th.join(timeout=15)
+        if self.enabled:
+            self.th.join(timeout=15)
 
     def summary(self):
         if not self.vals:
@@ -345,6 +347,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-causal", action="store_true", help="skip the causal-mask leg")
     ap.add_argument("--no-prologue", action="store_true", help="skip the fused-prologue timing")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="do not sample the clock with amd-smi (under a counter-collecting profiler, whose "
+                         "preloaded library makes the sampler's child process unable to start)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration for profiles)")
@@ -392,7 +397,7 @@ def main():
     clocks = None
     for vw in variants:
         print(f"[bench] fused {vw.name}", file=sys.stderr, flush=True)
-        with ClockSampler() as cs:
+        with ClockSampler(enabled=not args.no_sclk) as cs:
             st_ms, fwd_ms, fwd_max, fwd_mean, q_ms, out, counts = time_path(fs, W, vw, q, k, v, args.steps if vw is w else
                                                                   max(3, args.steps // 2), args.warmup)
         if vw is w:
