@@ -182,16 +182,20 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
   const int grp = lane >> 4, jl = lane & 15;
   const int vrow0 = 8 * (grp >> 1) + (jl >> 2);                    // + 16 t + 4 half
   const int vcol = 2 * (16 * (grp & 1) + 4 * (jl & 3));             // bytes within the block's 64
-  auto v_op = [&](uint32_t vslot, int t, int o) -> v8bf {
-    v4s16 r2[2];
+  // the lane's byte offset of block o in a slot (rows 16 t + 4 half + vrow0
+  // share vrow0's swizzle), so that each read adds only a constant
+  uint32_t voff[NO];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int row = 16 * t + 4 * half + vrow0;
-      const int byte = 64 * o + vcol;  // chunk byte / 16, 8-byte half (byte / 8) % 2
-      const uint32_t off = (uint32_t)(row * G::ROW + 16 * ((byte >> 4) ^ vswz<D>(row)) + (byte & 15));
-      r2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(size_t)(vslot + off));
-    }
-    return __builtin_bit_cast(v8bf, __builtin_shufflevector(r2[0], r2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  for (int o = 0; o < NO; ++o) {
+    const int byte = 64 * o + vcol;  // chunk byte / 16, 8-byte half (byte / 8) % 2
+    voff[o] = (uint32_t)(vrow0 * G::ROW + 16 * ((byte >> 4) ^ vswz<D>(vrow0)) + (byte & 15));
+  }
+  auto v_op = [&](const uint32_t (&vb)[NO], int t, int o) -> v8bf {
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    const lds_u8* base = (const lds_u8*)(size_t)vb[o];
+    const v4s16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(base + 16 * t * G::ROW));
+    const v4s16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(base + (16 * t + 4) * G::ROW));
+    return __builtin_bit_cast(v8bf, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
   // ---- Q^T operands (B of S^T): lane (q, h), chunk c: Q[q][16c + 8h .. +8]
@@ -299,11 +303,14 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
     lsum += (lp[0] + lp[1]) + (lp[2] + lp[3]);
     // ---- O += P V: chunk t = 2 kg + (i / 2) holds registers 8t .. 8t + 7
     const uint32_t vslot = lds0 + (uint32_t)(G::V_OFF + slot * G::VSLOT);
+    uint32_t vb[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) vb[o] = vslot + voff[o];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const v8bf pa = __builtin_bit_cast(v8bf, uint4{pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]});
 #pragma unroll
-      for (int o = 0; o < NO; ++o) O[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, v_op(vslot, t, o), O[o], 0, 0, 0);
+      for (int o = 0; o < NO; ++o) O[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, v_op(vb, t, o), O[o], 0, 0, 0);
     }
   }
   wait_vm<0>();  // loads past the end are still in flight
