@@ -212,6 +212,8 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
   for (int o = 0; o < NO; ++o)
 #pragma unroll
     for (int e = 0; e < 16; ++e) O[o][e] = 0.0f;
+  // byte address of lane ^ 32 (the other half of the query's keys), for ds_bpermute
+  const int xhalf = (lane ^ 32) << 2;
   float m = -INFINITY;  // running max of query n (scaled, log2 units), lanes n and n + 32 agree
   float lsum = 0.0f;    // this lane's share of the row sum
 
@@ -264,7 +266,7 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
     for (int i = 2; i < 32; i += 2)
       mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, S[i >> 4][i & 15]), S[i >> 4][(i + 1) & 15]);
     mx *= c_log2;
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = __builtin_fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xhalf, __float_as_int(mx))));
     const float mnew = __builtin_fmaxf(m, mx);
     if (__ballot(mnew > m) != 0) {
       // the reference grows: rescale O and l by exp2(m_old - m_new)
