@@ -324,16 +324,34 @@ __device__ __forceinline__ void p_from_w(const uint32_t (&w)[16], float m0, floa
     dsc[0] = sc;
     dsc[1] = sc;
   } else {
-    const float b0m = __builtin_fmaxf(m0, wshfl(m0, lane ^ 32));
-    const float b1m = __builtin_fmaxf(m1, wshfl(m1, lane ^ 32));
-    const uint32_t b0 = (b0m >= 128.0f) ? min(__float2uint_rz(b0m), 0x7F7Fu) : 0u;
-    const uint32_t b1 = (b1m >= 128.0f) ? min(__float2uint_rz(b1m), 0x7F7Fu) : 0u;
-    const uint32_t s0 = p_scale<PE>(b0), s1 = p_scale<PE>(b1);
-    const float X0 = e8m0_to_float(s0), X1 = e8m0_to_float(s1);
+    const float b0m = vmax(m0, wshfl(m0, lane ^ 32));
+    const float b1m = vmax(m1, wshfl(m1, lane ^ 32));
+    uint32_t s0, s1;
+    float X0, X1;
+    if constexpr (FAST) {
+      // both block maxima lie in [PFlush, TgEff]: the fma form of the fast
+      // path above, no flush, clamp or zero scale
+      constexpr int thr7 = (int)(Fmt<PE>::mthr23 >> 16);
+      constexpr float off = (float)(127 - thr7) / 128.0f - (float)Fmt<PE>::emax;
+      s0 = __float2uint_rz(__builtin_fmaf(b0m, 1.0f / 128.0f, off));
+      s1 = __float2uint_rz(__builtin_fmaf(b1m, 1.0f / 128.0f, off));
+      X0 = __uint_as_float(s0 << 23);
+      X1 = __uint_as_float(s1 << 23);
+    } else {
+      const uint32_t b0 = (b0m >= 128.0f) ? min(__float2uint_rz(b0m), 0x7F7Fu) : 0u;
+      const uint32_t b1 = (b1m >= 128.0f) ? min(__float2uint_rz(b1m), 0x7F7Fu) : 0u;
+      s0 = p_scale<PE>(b0);
+      s1 = p_scale<PE>(b1);
+      X0 = e8m0_to_float(s0);
+      X1 = e8m0_to_float(s1);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float Xi = (i < 4) ? X0 : X1;
-      v2s r = {0, 0};
+      // the two converts write both halves of r, so r may start as any
+      // value: the patterns word it converts first, which dies there (no
+      // register has to be cleared)
+      v2s r = __builtin_bit_cast(v2s, w[2 * i]);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf, w[2 * i]), Xi, false);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf, w[2 * i + 1]), Xi, true);
       pA[i] = (int)((uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16));
@@ -796,7 +814,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     const float m0 = max16(S[0]), m1 = max16(S[1]);
     float tm, lo;
     if constexpr (Opd<PE>::split) {
-      const float b0 = __builtin_fmaxf(m0, wshfl(m0, lane ^ 32)), b1 = __builtin_fmaxf(m1, wshfl(m1, lane ^ 32));
+      const float b0 = vmax(m0, wshfl(m0, lane ^ 32)), b1 = vmax(m1, wshfl(m1, lane ^ 32));
       lo = __builtin_fminf(b0, b1);
       tm = __builtin_fmaxf(b0, b1);
     } else {
