@@ -409,6 +409,8 @@ def main():
                "rollbacks": int(counts.sum().item())}
         if bf16_ms is not None:
             rec["speedup_vs_bf16_kernel"] = round(bf16_ms / fwd_ms, 3)
+            # the denominator's own utilisation, beside every speedup
+            rec["bf16_kernel_util"] = round(vw.flops / (bf16_ms * 1e-3) / 1e12 / PEAK["bf16"], 4)
             rec["speedup_vs_bf16_incl_quant"] = round(bf16_ms / st_ms, 3)
         formats[vw.name] = rec
         if vw is w:
