@@ -94,6 +94,25 @@ __device__ __forceinline__ uint32_t quant_block(float* x, bool fitmax, uint32_t*
   return code;
 }
 
+// Non-temporal form for outputs written as whole contiguous runs (axis 0:
+// a wave writes 64 consecutive blocks), which no later step of the kernel
+// reads: streamed past the caches.  Measured on the video shape: FP6 and FP4
+// blocks 2-4 % faster, FP8 blocks 2 % slower; the axis-1 outputs (96-byte
+// runs, partial lines) 50 % slower, so they keep ordinary stores.
+typedef unsigned v4u_st __attribute__((ext_vector_type(4)));
+typedef unsigned v2u_st __attribute__((ext_vector_type(2)));
+template <int BYTES>
+__device__ __forceinline__ void store_block_nt(uint8_t* dst, const uint32_t* w) {
+  if constexpr (BYTES == 24) {
+    v2u_st* d = reinterpret_cast<v2u_st*>(dst);
+    __builtin_nontemporal_store((v2u_st){w[0], w[1]}, d);
+    __builtin_nontemporal_store((v2u_st){w[2], w[3]}, d + 1);
+    __builtin_nontemporal_store((v2u_st){w[4], w[5]}, d + 2);
+  } else {
+    __builtin_nontemporal_store((v4u_st){w[0], w[1], w[2], w[3]}, reinterpret_cast<v4u_st*>(dst));
+  }
+}
+
 template <int BYTES>
 __device__ __forceinline__ void store_block(uint8_t* dst, const uint32_t* w) {
   if constexpr (BYTES == 32) {
@@ -140,7 +159,9 @@ __global__ void __launch_bounds__(256) mxq_axis0_kernel(const uint16_t* __restri
   }
   uint32_t w[8];
   uint32_t code = quant_block<ELEM>(x, fitmax, w, prescale == 1.0f);
-  store_block<BB>(codes + blk * BB, w);
+  // FP6/FP4 blocks leave faster past the caches; 32-byte FP8 blocks do not
+  if constexpr (BB < 32) store_block_nt<BB>(codes + blk * BB, w);
+  else store_block<BB>(codes + blk * BB, w);
   scales[blk] = (uint8_t)code;
 }
 
