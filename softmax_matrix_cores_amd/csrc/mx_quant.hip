@@ -301,10 +301,22 @@ __global__ void __launch_bounds__(AX1_TB) mxq_axis1_direct_kernel(const uint16_t
   const int co = lane % LPB;
   const uint16_t* p = src + (m * rows + kb * 32) * ld + 8 * co;
   const int nrow = (int)min((int64_t)32, rows - kb * 32);
+  // rows are read once: for the FP6/FP4 outputs, non-temporal loads (past
+  // the caches) are faster on the video V (FP6 6 %, FP4 18 %); for FP8 they
+  // are 4 % slower, and on the axis-0 kernel 40 % slower
+  constexpr bool NT = Fmt<ELEM>::bits < 8;
+  typedef unsigned v4u_ld __attribute__((ext_vector_type(4)));
   uint4 r[32];
 #pragma unroll
-  for (int j = 0; j < 32; ++j)
-    r[j] = j < nrow ? *reinterpret_cast<const uint4*>(p + (int64_t)j * ld) : make_uint4(0u, 0u, 0u, 0u);
+  for (int j = 0; j < 32; ++j) {
+    if (j < nrow) {
+      const v4u_ld* a = reinterpret_cast<const v4u_ld*>(p + (int64_t)j * ld);
+      const v4u_ld t = NT ? __builtin_nontemporal_load(a) : *a;
+      r[j] = make_uint4(t[0], t[1], t[2], t[3]);
+    } else {
+      r[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   const bool exact = prescale == 1.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

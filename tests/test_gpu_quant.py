@@ -41,3 +41,33 @@ def test_quantizer_bytes(oracle, elem, rule, axis):
     torch.cuda.synchronize()
     o = oracle.quantize_mx(bits(x), axis, oracle.ELEM_NAMES[elem], prescale=pre, rule=rule)
     assert same_bytes(g, o, axis=axis) == (True, True)
+
+
+# axis-1 shapes beyond the video case, through the C ABI: D = 64 and a
+# prescale (the direct kernel's two paths), column counts 96 and 32 (the
+# generic kernel), a key count below one block, and rows ld = cols + 4
+# elements apart (unaligned rows: the generic kernel)
+AX1_SHAPES = [(77, 64, 1.0, 0), (100, 128, 0.75, 0), (45, 96, 1.0, 0), (20, 32, 1.5, 0), (70, 128, 1.0, 4)]
+
+
+@pytest.mark.parametrize("shape", AX1_SHAPES, ids=[f"r{r}c{c}p{p}ld{e}" for r, c, p, e in AX1_SHAPES])
+@pytest.mark.parametrize("elem", ELEMS)
+def test_quantizer_axis1_shapes(oracle, elem, shape):
+    import ctypes
+
+    rows, cols, pre, extra = shape
+    n, ld = 2, cols + extra
+    x = _inputs(n, rows, ld, 300 + ELEMS.index(elem) + rows)
+    log(f"[quant] axis1 {elem} rows={rows} cols={cols} prescale={pre} ld={ld}")
+    e = fs.ELEMS[elem]
+    cb, sb = fs.mx_sizes(e, n, rows, cols, 1)
+    codes = torch.zeros(cb, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(sb, dtype=torch.uint8, device="cuda")
+    xd = x.cuda()
+    st = fs.lib().fsattn_quantize_mx(xd.data_ptr(), n, rows, cols, ld, 1, ctypes.c_float(pre), e, fs.SCALE_FITMAX,
+                                     codes.data_ptr(), scales.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, fs.lib().fsattn_status_str(st)
+    torch.cuda.synchronize()
+    o = oracle.quantize_mx(bits(x[..., :cols]), 1, oracle.ELEM_NAMES[elem], prescale=pre)
+    g = fs.MXTensor(codes, scales, e, pre)
+    assert same_bytes(g, o, axis=1) == (True, True)
