@@ -41,8 +41,9 @@
 //     its PV instructions, picked with op_sel.
 //   * fast path per score: one float->int convert (stage 1; the odd score of
 //     a pair converts straight into the high half of the packed word) and
-//     half a max3.  The E8M0 of P comes from the block max with integer
-//     exponent arithmetic; one v_cvt_scalef32_pk32_fp6_bf16 converts a lane's
+//     half a max3.  The E8M0 of P comes from the block max with one fma and
+//     a convert (the exact path: integer exponent arithmetic on the block's
+//     largest pattern); one v_cvt_scalef32_pk32_fp6_bf16 converts a lane's
 //     32 keys.  A wave ballot sends a step to the exact path on the first
 //     step, a step holding a masked key (past the batch's key count, or past
 //     a row's causal limit), a possible gate fire or stage-1 clamp, or a
