@@ -285,6 +285,32 @@ def time_bf16(fs, w, q, k, v, steps, warmup, causal=False):
     return statistics.median(ts), out
 
 
+def time_torch_sdpa(w, q, k, v):
+    """Context for the BF16 denominator: PyTorch's scaled_dot_product_attention on the same bf16
+    inputs, flash backend only (never the math backend, which would materialise the scores).
+    Returns (median ms of 2 timed calls, backend) or None when the backend is unavailable."""
+    import torch
+    import torch.nn.functional as F
+
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            F.scaled_dot_product_attention(q, k, v, scale=w.sigma)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(2):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                F.scaled_dot_product_attention(q, k, v, scale=w.sigma)
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+        return statistics.median(ts), "flash"
+    except Exception:  # no flash backend in this torch build: no context figure
+        return None
+
+
 def cpu_baseline(w, q, k, v, budget_s: float = 15.0):
     """The oracle on sampled query rows of one head, in attention TFLOPS."""
     import numpy as np
@@ -345,6 +371,7 @@ def main():
     ap.add_argument("--also", default="auto", help="other formats of the same shape (auto: the video pair)")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sdpa", action="store_true", help="skip the PyTorch SDPA context figure")
     ap.add_argument("--no-causal", action="store_true", help="skip the causal-mask leg")
     ap.add_argument("--no-prologue", action="store_true", help="skip the fused-prologue timing")
     ap.add_argument("--no-sclk", action="store_true",
@@ -488,6 +515,15 @@ def main():
         line["bf16_baseline"] = {"kernel_ms": round(bf16_ms, 4), "tflops": round(bt, 2),
                                  "bf16_mfma_util": round(bt / PEAK["bf16"], 4),
                                  "util_vs_measured_peak": round(bt / probes["bf16"]["tflops"], 4)}
+        if not args.no_sdpa:
+            print("[bench] torch sdpa (context)", file=sys.stderr, flush=True)
+            r = time_torch_sdpa(w, q, k, v)
+            if r is not None:
+                line["bf16_baseline"]["context_torch_sdpa"] = {
+                    "backend": r[1], "kernel_ms": round(r[0], 3),
+                    "tflops": round(w.flops / (r[0] * 1e-3) / 1e12, 1),
+                    "in_library_bf16_speedup": round(r[0] / bf16_ms, 3),
+                    "fused_speedup": round(r[0] / fwd_ms, 3)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
