@@ -131,7 +131,10 @@ __device__ __forceinline__ void store_block(uint8_t* dst, const uint32_t* w) {
 
 // axis 0: one lane per 32-element block of a row; blocks are contiguous in
 // both the input row and the packed output.
-template <int ELEM, bool VEC>
+// EXACT: prescale is 1, so every value is an exact bf16 (no product, and the
+// FP6 path needs no rounding to odd); chosen on the host, which keeps the
+// other form's arithmetic out of the kernel.
+template <int ELEM, bool VEC, bool EXACT>
 __global__ void __launch_bounds__(256) mxq_axis0_kernel(const uint16_t* __restrict__ src, int64_t nrows,
                                                         int64_t nb, int64_t ld, float prescale, bool fitmax,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
@@ -149,16 +152,20 @@ __global__ void __launch_bounds__(256) mxq_axis0_kernel(const uint16_t* __restri
       uint32_t uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[8 * i + 2 * j] = bf16_to_f32(uu[j] & 0xFFFFu) * prescale;
-        x[8 * i + 2 * j + 1] = bf16_to_f32(uu[j] >> 16) * prescale;
+        x[8 * i + 2 * j] = bf16_to_f32(uu[j] & 0xFFFFu);
+        x[8 * i + 2 * j + 1] = bf16_to_f32(uu[j] >> 16);
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = bf16_to_f32(p[i]) * prescale;
+    for (int i = 0; i < 32; ++i) x[i] = bf16_to_f32(p[i]);
+  }
+  if constexpr (!EXACT) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] *= prescale;
   }
   uint32_t w[8];
-  uint32_t code = quant_block<ELEM>(x, fitmax, w, prescale == 1.0f);
+  uint32_t code = quant_block<ELEM>(x, fitmax, w, EXACT);
   // FP6/FP4 blocks leave faster past the caches; 32-byte FP8 blocks do not
   if constexpr (BB < 32) store_block_nt<BB>(codes + blk * BB, w);
   else store_block<BB>(codes + blk * BB, w);
@@ -278,60 +285,112 @@ __global__ void __launch_bounds__(256) mxq_axis1_kernel(const uint16_t* __restri
 // column octet co) loads 16 bytes (8 columns) of each of the block's 32 key
 // rows and quantizes the eight column blocks from registers.  The COLS / 8
 // lanes of one key block read whole rows (a wave covers 64 / (COLS / 8)
-// consecutive key blocks), and every lane has 32 loads in flight before it
-// converts.  Neighbouring key blocks of a column are written by neighbouring
-// lane groups, as contiguous runs.  The arithmetic per block is the same as
-// mxq_axis1_kernel's (same quant_block, zero padding past the last key).
+// consecutive key blocks, a workgroup KBG = 4 such groups of one matrix), and
+// every lane has 32 loads in flight before it converts.  The arithmetic per
+// block is the same as mxq_axis1_kernel's (same quant_block, zero padding past
+// the last key).
+//
+// Output: column d's KBG blocks are one contiguous run of the codes
+// ([m][d][kb] blocks), and the KBG key blocks' scales one contiguous range
+// ([m][kb][32][4]).  A lane's own blocks lie in eight different runs, so the
+// workgroup first places its blocks and scales in LDS in output order and
+// then writes every run with consecutive lanes on consecutive 8- or 16-byte
+// pieces (a few cache lines per store instruction instead of 16-32).  On the
+// video V this and the EXACT form together take FP6 from 0.230 to 0.219 ms,
+// FP8 from 0.249 to 0.232 and FP4 from 0.176 to 0.169; non-temporal stores of
+// the runs are slower for FP6 and FP4 (2 % and 11 %).
 constexpr int AX1_TB = 256;  // threads per workgroup
 template <int ELEM, int COLS>
+struct Ax1Stage {
+  // columns per lane: 8 (16-byte loads); 4 columns per lane (more waves per
+  // SIMD, half the registers) measured 3 % slower for FP6, 16 % for FP8
+  static constexpr int CPL = 8;
+  static constexpr int BB = Fmt<ELEM>::bits * 4;  // bytes per block
+  static constexpr int LPB = COLS / CPL;           // lanes per key block
+  static constexpr int KBW = 64 / LPB;             // key blocks per wave
+  static constexpr int KBG = 4 * KBW;              // key blocks per workgroup
+  static constexpr int RUN = KBG * BB;             // bytes of one column's run
+  static constexpr int CH = (BB % 16 == 0) ? 16 : 8;  // output piece (divides BB; runs are CH-aligned)
+  // LDS row pitch: the run plus one piece (the lanes of one key block write
+  // rows 8 apart; the pad spreads them over several bank offsets)
+  static constexpr int PITCH = RUN + CH;
+  static constexpr int SC = KBG * 128;                // scale bytes of the workgroup
+  static constexpr int LDS = COLS * PITCH + SC;
+};
+template <int ELEM, int COLS, bool EXACT>
 __global__ void __launch_bounds__(AX1_TB) mxq_axis1_direct_kernel(const uint16_t* __restrict__ src, int64_t n_mat,
                                                                   int64_t rows, int64_t ld, int64_t nb,
                                                                   float prescale, bool fitmax,
                                                                   uint8_t* __restrict__ codes,
                                                                   uint8_t* __restrict__ scales) {
-  constexpr int BB = Fmt<ELEM>::bits * 4;
-  constexpr int LPB = COLS / 8;   // lanes per key block
-  constexpr int KBW = 64 / LPB;   // key blocks per wave
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * AX1_TB + threadIdx.x) >> 6;
-  const int64_t wpm = (nb + KBW - 1) / KBW;  // waves per matrix
-  const int64_t m = wave / wpm;
-  const int64_t kb = (wave - m * wpm) * KBW + lane / LPB;
-  if (m >= n_mat || kb >= nb) return;
-  const int co = lane % LPB;
-  const uint16_t* p = src + (m * rows + kb * 32) * ld + 8 * co;
-  const int nrow = (int)min((int64_t)32, rows - kb * 32);
-  // rows are read once: for the FP6/FP4 outputs, non-temporal loads (past
-  // the caches) are faster on the video V (FP6 6 %, FP4 18 %); for FP8 they
-  // are 4 % slower, and on the axis-0 kernel 40 % slower
-  constexpr bool NT = Fmt<ELEM>::bits < 8;
-  typedef unsigned v4u_ld __attribute__((ext_vector_type(4)));
-  uint4 r[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    if (j < nrow) {
-      const v4u_ld* a = reinterpret_cast<const v4u_ld*>(p + (int64_t)j * ld);
-      const v4u_ld t = NT ? __builtin_nontemporal_load(a) : *a;
-      r[j] = make_uint4(t[0], t[1], t[2], t[3]);
-    } else {
-      r[j] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  const bool exact = prescale == 1.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float x[32];
+  using G = Ax1Stage<ELEM, COLS>;
+  constexpr int BB = G::BB;
+  __shared__ __align__(16) uint8_t stage[G::LDS];
+  uint8_t* sscale = stage + COLS * G::PITCH;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t wgm = (nb + G::KBG - 1) / G::KBG;  // workgroups per matrix
+  const int64_t m = blockIdx.x / wgm;
+  const int64_t kb0 = (blockIdx.x - m * wgm) * G::KBG;
+  const int kbl = wv * G::KBW + lane / G::LPB;  // the lane's key block within the workgroup
+  const int64_t kb = kb0 + kbl;
+  // the grid holds whole matrices only (m < n_mat); lanes past the last key
+  // block convert nothing but still take part in the barrier
+  if (kb < nb) {
+    const int co = lane % G::LPB;
+    const uint16_t* p = src + (m * rows + kb * 32) * ld + G::CPL * co;
+    const int nrow = (int)min((int64_t)32, rows - kb * 32);
+    // rows are read once: for the FP6/FP4 outputs, non-temporal loads (past
+    // the caches) are faster on the video V (FP6 6 %, FP4 18 %); for FP8 they
+    // are 4 % slower, and on the axis-0 kernel 40 % slower
+    constexpr bool NT = Fmt<ELEM>::bits < 8;
+    typedef unsigned vld __attribute__((ext_vector_type(G::CPL / 2)));
+    vld r[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const uint32_t wv = (e < 2) ? r[j].x : (e < 4) ? r[j].y : (e < 6) ? r[j].z : r[j].w;
-      const float f = bf16_to_f32((e & 1) ? (wv >> 16) : (wv & 0xFFFFu));
-      x[j] = exact ? f : f * prescale;
+      if (j < nrow) {
+        const vld* a = reinterpret_cast<const vld*>(p + (int64_t)j * ld);
+        r[j] = NT ? __builtin_nontemporal_load(a) : *a;
+      } else {
+        r[j] = (vld)(0u);
+      }
     }
-    uint32_t w[8];
-    const uint32_t code = quant_block<ELEM>(x, fitmax, w, exact);
-    const int d = 8 * co + e;
-    store_block<BB>(codes + ((m * COLS + d) * nb + kb) * BB, w);
-    scales[((m * nb + kb) * 32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)code;
+#pragma unroll
+    for (int e = 0; e < G::CPL; ++e) {
+      float x[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint32_t wd = r[j][e >> 1];
+        const float f = bf16_to_f32((e & 1) ? (wd >> 16) : (wd & 0xFFFFu));
+        x[j] = EXACT ? f : f * prescale;
+      }
+      uint32_t w[8];
+      const uint32_t code = quant_block<ELEM>(x, fitmax, w, EXACT);
+      const int d = G::CPL * co + e;
+      uint2* q = reinterpret_cast<uint2*>(stage + d * G::PITCH + kbl * BB);
+#pragma unroll
+      for (int i = 0; i < BB / 8; ++i) q[i] = make_uint2(w[2 * i], w[2 * i + 1]);
+      if constexpr (COLS == 128) sscale[kbl * 128 + (d & 31) * 4 + (d >> 5)] = (uint8_t)code;
+      else scales[((m * nb + kb) * 32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)code;
+    }
+  }
+  __syncthreads();
+  // the runs: piece pc of column d lies in key block kb0 + (pc * CH) / BB (CH
+  // divides BB), and is written when that key block exists
+  const int nvalid = (int)min((int64_t)G::KBG, nb - kb0);
+  constexpr int PPR = G::RUN / G::CH;  // pieces per run
+  for (int c = threadIdx.x; c < COLS * PPR; c += AX1_TB) {
+    const int d = c / PPR, pc = c - d * PPR;
+    if ((pc * G::CH) / BB >= nvalid) continue;
+    uint8_t* dst = codes + ((m * COLS + d) * nb + kb0) * BB + pc * G::CH;
+    const uint8_t* sp = stage + d * G::PITCH + pc * G::CH;
+    if constexpr (G::CH == 16) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(sp);
+    else *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(sp);
+  }
+  if constexpr (COLS == 128) {
+    // 128 scale bytes per key block, contiguous over the workgroup's blocks
+    for (int c = threadIdx.x; c < nvalid * 8; c += AX1_TB)
+      *reinterpret_cast<uint4*>(scales + (m * nb + kb0) * 128 + 16 * c) =
+          *reinterpret_cast<const uint4*>(sscale + 16 * c);
   }
 }
 
@@ -344,26 +403,36 @@ static hipError_t launch_elem(const uint16_t* src, int64_t n_mat, int64_t rows, 
     int64_t nb = cols / 32, total = n_mat * rows * nb;
     dim3 grid((unsigned)((total + TB - 1) / TB));
     bool vec = (ld % 8 == 0) && ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
-    if (vec)
-      hipLaunchKernelGGL((mxq_axis0_kernel<ELEM, true>), grid, dim3(TB), 0, stream, src, n_mat * rows, nb, ld,
-                         prescale, fitmax, codes, scales);
-    else
-      hipLaunchKernelGGL((mxq_axis0_kernel<ELEM, false>), grid, dim3(TB), 0, stream, src, n_mat * rows, nb, ld,
-                         prescale, fitmax, codes, scales);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(TB), 0, stream, src, n_mat * rows, nb, ld, prescale, fitmax, codes, scales);
+    };
+    if (vec) {
+      if (prescale == 1.0f) go(mxq_axis0_kernel<ELEM, true, true>);
+      else go(mxq_axis0_kernel<ELEM, true, false>);
+    } else {
+      if (prescale == 1.0f) go(mxq_axis0_kernel<ELEM, false, true>);
+      else go(mxq_axis0_kernel<ELEM, false, false>);
+    }
   } else {
     int64_t nb = (rows + 31) / 32, total = n_mat * nb * cols;
     const bool direct = (cols == 64 || cols == 128) && (ld % 8 == 0) &&
-                        ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
+                        ((reinterpret_cast<uintptr_t>(src) & 15) == 0) &&
+                        ((reinterpret_cast<uintptr_t>(scales) & 15) == 0);
     if (direct) {
-      const int kbw = 64 / (int)(cols / 8);
-      const int64_t waves = n_mat * ((nb + kbw - 1) / kbw);
-      dim3 grid((unsigned)((waves * 64 + AX1_TB - 1) / AX1_TB));
-      if (cols == 128)
-        hipLaunchKernelGGL((mxq_axis1_direct_kernel<ELEM, 128>), grid, dim3(AX1_TB), 0, stream, src, n_mat, rows,
-                           ld, nb, prescale, fitmax, codes, scales);
-      else
-        hipLaunchKernelGGL((mxq_axis1_direct_kernel<ELEM, 64>), grid, dim3(AX1_TB), 0, stream, src, n_mat, rows,
-                           ld, nb, prescale, fitmax, codes, scales);
+      const int kbg = 4 * (64 / (int)(cols / 8));  // key blocks per workgroup
+      dim3 grid((unsigned)(n_mat * ((nb + kbg - 1) / kbg)));
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(AX1_TB), 0, stream, src, n_mat, rows, ld, nb, prescale, fitmax, codes,
+                           scales);
+      };
+      const bool ex = prescale == 1.0f;
+      if (cols == 128) {
+        if (ex) go(mxq_axis1_direct_kernel<ELEM, 128, true>);
+        else go(mxq_axis1_direct_kernel<ELEM, 128, false>);
+      } else {
+        if (ex) go(mxq_axis1_direct_kernel<ELEM, 64, true>);
+        else go(mxq_axis1_direct_kernel<ELEM, 64, false>);
+      }
     } else {
       dim3 grid((unsigned)((total + TB - 1) / TB));
       hipLaunchKernelGGL((mxq_axis1_kernel<ELEM>), grid, dim3(TB), 0, stream, src, n_mat, rows, cols, ld, nb,
