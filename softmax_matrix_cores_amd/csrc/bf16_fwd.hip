@@ -206,6 +206,14 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
 #pragma unroll
     for (int c = 0; c < NC; ++c) qB[c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qp + 16 * c + 8 * hh));
   }
+  // the Q loads land before any DMA is issued: their first use is inside the
+  // step loop, and the waits the compiler places before a first use would
+  // otherwise sit in the loop body, where they count the step's own DMA
+  // loads as well (down to vmcnt 0: every step waited for the loads it had
+  // just issued).  The empty statements use the registers, so the compiler
+  // waits for the loads here, ahead of the DMA statements.
+#pragma unroll
+  for (int c = 0; c < NC; ++c) asm volatile("" ::"v"(qB[c]));
 
   v16f O[NO];
 #pragma unroll
