@@ -200,8 +200,10 @@ def time_path(fs, W, w, q, k, v, steps, warmup):
     return total / steps, statistics.median(fwd), max(fwd), statistics.mean(fwd), statistics.median(qnt), out, counts
 
 
-def time_fused_causal(fs, w, q, k, v, steps, warmup):
-    """Median fused-kernel time (ms) under a causal mask, HIP events on the launch stream."""
+def time_fused_causal(fs, w, q, k, v, steps, warmup, **fwd_kw):
+    """Median fused-kernel time (ms) under a causal mask, HIP events on the launch stream.
+    fwd_kw: further forward() arguments (fp8_products=True with causal=False: the
+    FP8-product path of E4M3 Q/K, unmasked)."""
     import torch
 
     st = torch.cuda.current_stream()
@@ -211,9 +213,11 @@ def time_fused_causal(fs, w, q, k, v, steps, warmup):
     out = torch.empty(w.B, w.H, w.Sq, w.D, dtype=torch.bfloat16, device=q.device)
     counts = torch.zeros(w.B, w.H, w.Sq, dtype=torch.int32, device=q.device)
 
+    kw = {"causal": True, **fwd_kw}
+
     def run():
         fs.forward(Q, K, V, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=w.tau, kv_tile=w.kv_tile,
-                   counts=counts, out=out, causal=True)
+                   counts=counts, out=out, **kw)
 
     for _ in range(warmup):
         run()
@@ -457,6 +461,19 @@ def main():
             cb_ms, _ = time_bf16(fs, w, q, k, v, max(3, args.steps // 2), 1, causal=True)
             formats[w.name + "-causal"]["bf16_causal_kernel_ms"] = round(cb_ms, 4)
             formats[w.name + "-causal"]["speedup_vs_bf16_causal_kernel"] = round(cb_ms / c_ms, 3)
+
+    if "video-mxfp8" in formats:
+        # E4M3 Q/K scores from the FP8 matrix core (fsattn_forward_fp8_products):
+        # faster, but its P codes do not meet the parity criterion
+        print("[bench] fused video-mxfp8, FP8 products", file=sys.stderr, flush=True)
+        w8 = W.WORKLOADS["video-mxfp8"]
+        p_ms, _ = time_fused_causal(fs, w8, q, k, v, max(3, args.steps // 2), 1, causal=False, fp8_products=True)
+        p_tf = w8.flops / (p_ms * 1e-3) / 1e12
+        rec8 = {"kernel_tflops": round(p_tf, 2), "kernel_ms": round(p_ms, 4), "mx_mfma_util": round(p_tf / _peak_for(w8), 4),
+                "note": "scores from the FP8 matrix core; P codes differ from the definition (up to 1.3e-3 measured)"}
+        if bf16_ms is not None:
+            rec8["speedup_vs_bf16_kernel"] = round(bf16_ms / p_ms, 3)
+        formats["video-mxfp8-fp8-products"] = rec8
 
     if not args.no_prologue and w.name.startswith("video-"):
         print("[bench] fused prologue", file=sys.stderr, flush=True)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define FSATTN_ABI_VERSION 2
+#define FSATTN_ABI_VERSION 3
 
 typedef enum {
   FSATTN_OK = 0,
@@ -200,6 +200,9 @@ typedef struct {
  *   stage 1: b = floor(t) as a BF16 bit pattern (0 if t < 128, at most 0x7F7F)
  *   stage 2: P = MX(bf16(b)) per 32 consecutive keys (fit-max E8M0)
  *   O_i += P V, l_i += P 1 (same P); finally O_i / l_i rounded to bf16.
+ * FP6/FP4 score products are exact on the matrix core.  E4M3 Q/K are
+ * decoded to BF16 (exact) and summed on the BF16 matrix core from zero, C_i
+ * added once in binary32; fsattn_forward_fp8_products keeps the FP8 product.
  * Errors: FSATTN_E_INVALID_ARG (null, sizes, D not 64/128, kv_tile not a
  * positive multiple of 32, tau < 0, bad enum, prescale/softmax_scale
  * mismatch, bad dump window), FSATTN_E_UNSUPPORTED (format combination,
@@ -242,6 +245,24 @@ typedef struct {
 
 int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
                           const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream);
+
+/*
+ * fsattn_forward_fp8_products -- fsattn_forward_masked (mask may be NULL)
+ * with E4M3 Q/K scores taken from the FP8 matrix core (the scaled 32x32x64
+ * f8f6f4 product with C_i as its initial value), the pages' kernel design
+ * for MXFP8 ("Fused-Softmax shifts an AI attention bottleneck onto faster
+ * GPU hardware", paragraphs 7-8).  gfx950's FP8 product does not return the
+ * correctly rounded sum: a score can differ from fl32(C_i + sum) by up to
+ * about D binary32 steps, and P codes of scores that close to a stage-1
+ * floor boundary can differ from the definition above (measured: up to
+ * 1.3e-3 of the codes).  fsattn_forward and fsattn_forward_masked instead
+ * decode E4M3 Q and K to BF16 (exact) and sum on the BF16 matrix core from
+ * zero, adding C_i once in binary32.  For other Q/K formats (exact on the
+ * matrix core) the two are the same.  Arguments, errors and layouts as
+ * fsattn_forward_masked.
+ */
+int fsattn_forward_fp8_products(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
+                                const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream);
 
 /*
  * fsattn_forward_efq -- the forward with P generated directly as MXFP4

@@ -27,6 +27,7 @@ ABI_SYMBOLS = (
     "fsattn_abi_version", "fsattn_status_str", "fsattn_mx_codes_bytes", "fsattn_mx_scales_bytes",
     "fsattn_quantize_mx", "fsattn_quantize_mx_rmsnorm", "fsattn_forward", "fsattn_forward_masked",
     "fsattn_forward_bf16_baseline", "fsattn_forward_bf16_baseline_masked", "fsattn_forward_efq",
+    "fsattn_forward_fp8_products",
     "fsattn_pattern_gate_tau", "fsattn_probe_mfma", "fsattn_fold_prescale",
 )
 
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
         L.fsattn_forward_masked.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_Mask),
                                             ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
                                             ctypes.POINTER(_MxTensor), V, V]
+        L.fsattn_forward_fp8_products.restype = I
+        L.fsattn_forward_fp8_products.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_Mask),
+                                                  ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
+                                                  ctypes.POINTER(_MxTensor), V, V]
         L.fsattn_forward_efq.restype = I
         L.fsattn_forward_efq.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_Mask), ctypes.c_float,
                                          ctypes.c_float, ctypes.POINTER(_MxTensor), ctypes.POINTER(_MxTensor),
@@ -232,7 +237,8 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
             p_elem, tau: float = 8.0, c: float = 0.0, kv_tile: int = 64, counts: torch.Tensor | None = None,
             out: torch.Tensor | None = None, p_dump: tuple | None = None, stream=None, causal: bool = False,
             q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None, efq_tau: float = EFQ_TAU,
-            efq_h: float = EFQ_H, gate: str = "exact", p_scale_rule: int = SCALE_FITMAX) -> torch.Tensor:
+            efq_h: float = EFQ_H, gate: str = "exact", p_scale_rule: int = SCALE_FITMAX,
+            fp8_products: bool = False) -> torch.Tensor:
     """Fused-Softmax attention forward.  Returns bf16 [B,H,Sq,D].
     counts: optional int32 [B,H,Sq] written with rollback counts.
     p_dump: optional (b, h, row0, row1, codes uint8 [rows, Skv32], scales uint8 [rows, Skv32/32]).
@@ -240,6 +246,8 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
     p_elem "e2m1": P straight from the scores by the EFQ-style rule with (efq_tau, efq_h)
     (fsattn_forward_efq).
     gate "pattern": the gate shortcut on stage-1 patterns (fsattn_pattern_gate_tau).
+    fp8_products: E4M3 Q/K scores from the FP8 matrix core (fsattn_forward_fp8_products) instead
+    of the exact BF16 decode.
     Every buffer is checked (dtype, device, contiguity, size) before the call."""
     dev = Q.codes.device
     if gate == "pattern":
@@ -284,6 +292,11 @@ def forward(Q: MXTensor, K: MXTensor, V: MXTensor, B: int, H: int, Sq: int, Skv:
                                       ctypes.c_float(efq_h), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                                       out.data_ptr(), _stream(stream))
         _check("fsattn_forward_efq", st)
+        return out
+    if fp8_products:
+        st = lib().fsattn_forward_fp8_products(ctypes.byref(p), ctypes.byref(m) if masked else None, ctypes.byref(q),
+                                               ctypes.byref(k), ctypes.byref(v), out.data_ptr(), _stream(stream))
+        _check("fsattn_forward_fp8_products", st)
         return out
     if masked:
         st = lib().fsattn_forward_masked(ctypes.byref(p), ctypes.byref(m), ctypes.byref(q), ctypes.byref(k),

@@ -125,10 +125,12 @@ int fsattn_quantize_mx_rmsnorm(const void* src, int64_t n_mat, int64_t rows, int
 }
 
 // the forward of every entry point; efq: E2M1 P by the EFQ-style rule with
-// (efq_tau, efq_h), else E2M1 P is refused (the two-stage path has no FP4 P)
+// (efq_tau, efq_h), else E2M1 P is refused (the two-stage path has no FP4 P);
+// fp8_products: E4M3 Q/K scores on the FP8 matrix core (else from operands
+// decoded to BF16)
 static int forward_impl(const fsattn_params* p, const fsattn_mask* mask, bool efq, float efq_tau, float efq_h,
-                        const fsattn_mx_tensor* q, const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out,
-                        void* stream) {
+                        bool fp8_products, const fsattn_mx_tensor* q, const fsattn_mx_tensor* k,
+                        const fsattn_mx_tensor* v, void* out, void* stream) {
   if (!p || !q || !k || !v) return FSATTN_E_INVALID_ARG;
   if (efq) {
     if (p->p_elem != FSATTN_E2M1) return FSATTN_E_INVALID_ARG;
@@ -206,6 +208,7 @@ static int forward_impl(const fsattn_params* p, const fsattn_mask* mask, bool ef
     a.efq_a = 0.0f;
   }
   a.efq_t128 = efq ? 128.0f * efq_tau : 0.0f;
+  a.fp8_products = fp8_products ? 1 : 0;
   hipError_t e = fsattn::launch_fsattn_fwd(a, p->B, p->D, q->elem, v->elem, p->p_elem,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FSATTN_OK : FSATTN_E_HIP;
@@ -213,12 +216,17 @@ static int forward_impl(const fsattn_params* p, const fsattn_mask* mask, bool ef
 
 int fsattn_forward_masked(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
                           const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream) {
-  return forward_impl(p, mask, false, 0.0f, 0.0f, q, k, v, out, stream);
+  return forward_impl(p, mask, false, 0.0f, 0.0f, false, q, k, v, out, stream);
+}
+
+int fsattn_forward_fp8_products(const fsattn_params* p, const fsattn_mask* mask, const fsattn_mx_tensor* q,
+                                const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out, void* stream) {
+  return forward_impl(p, mask, false, 0.0f, 0.0f, true, q, k, v, out, stream);
 }
 
 int fsattn_forward(const fsattn_params* p, const fsattn_mx_tensor* q, const fsattn_mx_tensor* k,
                    const fsattn_mx_tensor* v, void* out, void* stream) {
-  return forward_impl(p, nullptr, false, 0.0f, 0.0f, q, k, v, out, stream);
+  return forward_impl(p, nullptr, false, 0.0f, 0.0f, false, q, k, v, out, stream);
 }
 
 int fsattn_pattern_gate_tau(float tau, float schraudolph_c, float* tau_out) {
@@ -243,7 +251,7 @@ int fsattn_pattern_gate_tau(float tau, float schraudolph_c, float* tau_out) {
 int fsattn_forward_efq(const fsattn_params* p, const fsattn_mask* mask, float efq_tau, float efq_h,
                        const fsattn_mx_tensor* q, const fsattn_mx_tensor* k, const fsattn_mx_tensor* v, void* out,
                        void* stream) {
-  return forward_impl(p, mask, true, efq_tau, efq_h, q, k, v, out, stream);
+  return forward_impl(p, mask, true, efq_tau, efq_h, false, q, k, v, out, stream);
 }
 
 int fsattn_forward_bf16_baseline(const void* q, const void* k, const void* v, int B, int H, int Sq, int Skv, int D,

@@ -26,6 +26,15 @@
 //     initial value), O += P V (D/32 feature blocks).  l += P 1 uses one
 //     16x16x128 instruction whose ones operand selects, per output column, the
 //     lanes of one query (FP6 P), or a 32x32x64 ones operand (FP8 P).
+//   * E4M3 Q/K (X8): gfx950's FP8 product does not return the correctly
+//     rounded sum (a score can be off by up to about one binary32 step of
+//     the accumulator per product), which moves P codes of scores near a
+//     stage-1 floor boundary.  So the E4M3 K operands are decoded to BF16
+//     (exact: four significant bits times the block scale) on their way from
+//     LDS and multiplied with the Q operands decoded once at the start, on
+//     v_mfma_f32_32x32x16_bf16 (four per key group and feature half), summed
+//     from zero; C_i is added to each score once, in binary32.  The FP8
+//     product remains available (fsattn_forward_fp8_products).
 //   * the K rows of the score instructions are permuted so that a lane's 32
 //     scores are exactly the 32 keys of its P operand in the PV product.
 //   * K and V operands sit in an 8-slot LDS ring in operand order, so every
@@ -137,6 +146,18 @@ template <> struct PFlush<E4M3> { static constexpr float t = 2432.0f; };
 template <> struct PFlush<E3M2> { static constexpr float t = 1280.0f; };
 
 __device__ __forceinline__ float wshfl(float v, int src) { return __shfl(v, src, 64); }
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+// eight E4M3 codes (two dwords, byte order) times the block scale X, as BF16
+// (exact: four significant bits times a power of two, inside BF16's range
+// for every scale an operand of finite values gets)
+__device__ __forceinline__ v8bf dec8(int w0, int w1, float X) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w0, X, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w0, X, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w1, X, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w1, X, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 // One lane's MFMA operand from an LDS region in operand order
 template <int F> __device__ __forceinline__ v8i lds_operand(const uint8_t* region, int lane) {
@@ -516,8 +537,9 @@ __device__ __forceinline__ void rescale(v16f (&O)[NV], typename LAcc<PE>::T& L, 
   }
 }
 
-template <int QK, int VE, int PE, int D, bool KV128, bool DUMP>
+template <int QK, int VE, int PE, int D, bool KV128, bool DUMP, bool X8>
 __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
+  static_assert(!X8 || QK == E4M3, "decoded score products are for E4M3 Q/K");
   using G = Geo<QK, VE, D>;
   using LT = typename LAcc<PE>::T;
   using PT = typename POp<PE>::T;
@@ -648,13 +670,26 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       qS[dh] = (int)qsp[2 * dh + hh];
     }
   }
+  // X8: the Q operands decoded to BF16 (exact: 4 significant bits times a
+  // power of two), group c of feature half dh = dwords 2c, 2c+1 of qB[dh]
+  v8bf qX[X8 ? G::DH : 1][4];
+  if constexpr (X8) {
+    const int qrow = min(qw0 + n, Sq - 1);
+    const uint8_t* qsp = a.qs + ((size_t)bh * Sq + qrow) * G::KSB;
+#pragma unroll
+    for (int dh = 0; dh < G::DH; ++dh) {
+      const float s0 = e8m0_to_float(qsp[2 * dh]), s1 = e8m0_to_float(qsp[2 * dh + 1]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qX[dh][c] = dec8(qB[dh][2 * c], qB[dh][2 * c + 1], c < 2 ? s0 : s1);
+    }
+  }
   // K scale shift per key group: the dword holds the key's block scales
   // (D = 128) or those of an even/odd key pair (D = 64)
   int ksh[2];
 #pragma unroll
   for (int kg = 0; kg < 2; ++kg) {
     const int key = row_key<PE>(kg, n) + ko;
-    ksh[kg] = (D == 128) ? 8 * hh : 16 * (key & 1) + 8 * hh;
+    ksh[kg] = (D == 128 ? 0 : 16 * (key & 1)) + (X8 ? 0 : 8 * hh);
   }
   // ones operand of the l product.  FP6 P (16x16x128, lanes read as rows
   // l%16 and K blocks l/16): column c16 < 8 sums the blocks of query r
@@ -689,14 +724,20 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     else return mx - PFlush<PE>::t;
   };
 
+  // X8: the decoded score products start from zero and C is added to each
+  // score once, in binary32, after the products (fl32(fl32(sum) + C)); the
+  // sum is accumulated at its own magnitude, far below C's.  Otherwise C is
+  // the accumulator's initial value (FP6/FP4 products are exact).
   float C = 0.0f;
   v16f Cv;  // C splat: the accumulator's initial value of the score product
 #pragma unroll
   for (int k = 0; k < 16; ++k) Cv[k] = 0.0f;
   auto set_C = [&](float c) {
     C = c;
+    if constexpr (!X8) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) Cv[k] = c;
+      for (int k = 0; k < 16; ++k) Cv[k] = c;
+    }
   };
   int cnt = 0;
   v16f O[NV];
@@ -719,6 +760,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     KOps k;
     k.kd[0] = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 4 * n) >> ksh[0];
     k.kd[1] = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 128 + 4 * n) >> ksh[1];
+    // X8 (ksh without the lane half): byte b holds the scale of block b
 #pragma unroll
     for (int i = 0; i < 2 * G::DH; ++i) k.op[i] = lds_operand<QK>(slot + G::K_OFF + i * Opd<QK>::region, lane);
     return k;
@@ -726,6 +768,25 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   // S^T = K Q^T + C for the 64 keys of a step: both key groups' first
   // feature half (initial value C), then the second
   auto scores_of = [&](v16f (&S)[2], const KOps& k) {
+    if constexpr (X8) {
+      // decoded K groups against decoded Q groups on the BF16 matrix core:
+      // four 32x32x16 products per feature half and key group
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int dh = 0; dh < G::DH; ++dh) {
+          const v8i& ka = k.op[kg * G::DH + dh];
+          const float s0 = e8m0_to_float((k.kd[kg] >> (16 * dh)) & 0xFFu);
+          const float s1 = e8m0_to_float((k.kd[kg] >> (16 * dh + 8)) & 0xFFu);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const v8bf kx = dec8(ka[2 * c], ka[2 * c + 1], c < 2 ? s0 : s1);
+            if (dh == 0 && c == 0) S[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kx, qX[0][0], Cv, 0, 0, 0);
+            else S[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kx, qX[X8 ? dh : 0][c], S[kg], 0, 0, 0);
+          }
+        }
+      return;
+    }
 #pragma unroll
     for (int dh = 0; dh < G::DH; ++dh)
 #pragma unroll
@@ -790,7 +851,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     v16f Sn[2];
     scores(Sn, s);
     if (s >= ums) mask(Sn, lim - s * KS);
-    return max32(Sn);
+    // X8: max fl32(t + C) = fl32(max t + C), the map being monotonic
+    return X8 ? max32(Sn) + C : max32(Sn);
   };
 
   PT pA = {};
@@ -867,8 +929,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
       if (any_fire) {
         // in place: Cv holds C in every register
         C = C - delta;
+        if constexpr (!X8) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) Cv[k] = Cv[k] - delta;
+          for (int k = 0; k < 16; ++k) Cv[k] = Cv[k] - delta;
+        }
       }
     }
     if constexpr (EFQ) {
@@ -915,8 +979,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     any_fire = __ballot(fire) != 0;
     if (any_fire) {
       C = C - delta;
+      if constexpr (!X8) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) Cv[k] = Cv[k] - delta;
+        for (int k = 0; k < 16; ++k) Cv[k] = Cv[k] - delta;
+      }
     }
     if constexpr (EFQ) {
       p_efq<true>(S, m0, m1, T0, ea, et128, pA, pS, dsc);
@@ -982,6 +1048,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_s_setprio(3);
     if constexpr (PRE_V) pv_of(pA, pS, vop);
     else pv_of(pA, pS, read_v(u - 1));
+    if constexpr (X8) shift(S, C);
     const Check c = check(S, u, mn);
     const bool rare = (u >= ums) | (__ballot(c.bad) != 0);
     uint32_t dsc[2];
@@ -1047,23 +1114,31 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
   store_rows<NV, D>(a, bh, qw0, q_len, n, hh, O, lq, cnt);
 }
 
-template <int QK, int VE, int PE, int D>
+template <int QK, int VE, int PE, int D, bool X8>
 hipError_t launch_t(const FwdArgs& a, int B, hipStream_t stream) {
   dim3 grid((unsigned)((a.Sq + QWG - 1) / QWG), (unsigned)a.H, (unsigned)B);
   const bool dump = a.pd_codes != nullptr;
   if (a.kv128) {
-    if (dump) hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, true, true>), grid, dim3(NW * 64), 0, stream, a);
-    else hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, true, false>), grid, dim3(NW * 64), 0, stream, a);
+    if (dump) hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, true, true, X8>), grid, dim3(NW * 64), 0, stream, a);
+    else hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, true, false, X8>), grid, dim3(NW * 64), 0, stream, a);
   } else {
-    if (dump) hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, false, true>), grid, dim3(NW * 64), 0, stream, a);
-    else hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, false, false>), grid, dim3(NW * 64), 0, stream, a);
+    if (dump) hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, false, true, X8>), grid, dim3(NW * 64), 0, stream, a);
+    else hipLaunchKernelGGL((fsattn_fwd_kernel<QK, VE, PE, D, false, false, X8>), grid, dim3(NW * 64), 0, stream, a);
   }
   return hipGetLastError();
 }
 
+template <int QK, int VE, int PE, bool X8>
+hipError_t launch_x(const FwdArgs& a, int B, int D, hipStream_t s) {
+  return D == 128 ? launch_t<QK, VE, PE, 128, X8>(a, B, s) : launch_t<QK, VE, PE, 64, X8>(a, B, s);
+}
+// E4M3 Q/K: decoded BF16 score products unless the FP8 products are asked for
 template <int QK, int VE, int PE>
 hipError_t launch_d(const FwdArgs& a, int B, int D, hipStream_t s) {
-  return D == 128 ? launch_t<QK, VE, PE, 128>(a, B, s) : launch_t<QK, VE, PE, 64>(a, B, s);
+  if constexpr (QK == E4M3) {
+    if (!a.fp8_products) return launch_x<QK, VE, PE, true>(a, B, D, s);
+  }
+  return launch_x<QK, VE, PE, false>(a, B, D, s);
 }
 
 }  // namespace

@@ -27,6 +27,7 @@ struct FwdArgs {
   const int32_t* q_lens;   // [B] valid queries per batch, or null (Sq)
   const int32_t* kv_lens;  // [B] valid keys per batch, or null (Skv)
   float efq_a, efq_t128;   // E2M1 (EFQ-style) P: 1 / (128 h) rounded up, 128 tau
+  int fp8_products;        // E4M3 Q/K: score products on the FP8 matrix core (else decoded to BF16)
 };
 
 hipError_t launch_quantize_mx(const uint16_t* src, int64_t n_mat, int64_t rows, int64_t cols, int64_t ld, int axis,

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = fs.lib()
-    assert L.fsattn_abi_version() == 2
+    assert L.fsattn_abi_version() == 3
     for s in (0, -1, -2, -3, -4):
         assert L.fsattn_status_str(s)
     assert L.fsattn_status_str(-99) == b"unknown status"

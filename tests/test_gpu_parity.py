@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from softmax_matrix_cores_amd import workloads as W
-from tests.gpu_util import assert_ok, check_p, run_case
+from tests.gpu_util import assert_ok, check_p, check_p_fp8_products, run_case
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +87,23 @@ def test_stress_mxfp8_full(oracle):
     assert res["total_counts"] > 0
     assert_ok(res, defer_p=True)
     check_p(res)
+
+
+# E4M3 Q/K scores from the FP8 matrix core (fsattn_forward_fp8_products): every
+# criterion but the P-code one, which that path does not meet; there the
+# mismatch stays below the stated limit and every differing code is explained
+# by the products' rounding (explain_fp8)
+FP8P = [("stress", "stress-mxfp8", None), ("ragged", "stress-mxfp8", dict(B=1, H=2, Sq=97, Skv=300, D=128, seed=13)),
+        ("tau0", "stress-mxfp8", dict(B=1, H=2, Sq=96, Skv=520, D=128, seed=21, tau=0.0)),
+        ("d64", "tiny-mxfp8", dict(B=1, H=2, Sq=70, Skv=190, D=64, seed=14))]
+
+
+@pytest.mark.parametrize("name,base,kw", FP8P, ids=[f[0] for f in FP8P])
+def test_fp8_products_path(oracle, name, base, kw):
+    w = W.WORKLOADS[base] if kw is None else W.custom(base, name=f"fp8p-{name}", **kw)
+    res = run_case(oracle, w, dump_head=(0, w.H - 1), dump_rows=(0, w.Sq), fp8_products=True)
+    assert_ok(res, defer_p=True)
+    check_p_fp8_products(res)
 
 
 # the Schraudolph shift c != 0 (60801/8192, the RMS-optimal shift in BF16
