@@ -760,7 +760,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fsattn_fwd_kernel(FwdArgs a) {
     KOps k;
     k.kd[0] = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 4 * n) >> ksh[0];
     k.kd[1] = *reinterpret_cast<const uint32_t*>(slot + G::KS_OFF + 128 + 4 * n) >> ksh[1];
-    // X8 (ksh without the lane half): byte b holds the scale of block b
+    // with X8 (ksh without the lane half) byte b of kd holds the key's block b
+    // scale (D = 64: of blocks 0 and 1)
 #pragma unroll
     for (int i = 0; i < 2 * G::DH; ++i) k.op[i] = lds_operand<QK>(slot + G::K_OFF + i * Opd<QK>::region, lane);
     return k;
