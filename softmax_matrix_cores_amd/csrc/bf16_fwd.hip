@@ -7,8 +7,8 @@
 // (paragraph 5).  This kernel is that scheme, FlashAttention style:
 //   per 64-key step: s = q.k (BF16 MFMA, fp32 accumulate), running max m of
 //   s*sigma*log2e, p = exp2(s*sigma*log2e - m), O and l rescaled by
-//   exp2(m_old - m_new) when the max grows, O += bf16(p) V (BF16 MFMA),
-//   l += sum p; finally O / l.
+//   exp2(m_old - m_new) when the max grows (by more than 8, so p <= 2^8),
+//   O += bf16(p) V (BF16 MFMA), l += sum p; finally O / l.
 //
 // Mapping to CDNA4 (v_mfma_f32_32x32x16_bf16: lane (r = l%32, h = l/32) holds
 // row r, K elements [8h, 8h+8); accumulator lane (c, h) register 4i+j holds
@@ -276,8 +276,12 @@ __global__ void __launch_bounds__(BW * 64, 1) bf16_fwd_kernel(const uint16_t* __
     mx *= c_log2;
     mx = __builtin_fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xhalf, __float_as_int(mx))));
     const float mnew = __builtin_fmaxf(m, mx);
-    if (__ballot(mnew > m) != 0) {
-      // the reference grows: rescale O and l by exp2(m_old - m_new)
+    // the reference moves only when some row's maximum grows by more than 8
+    // (a factor of 256; FlashAttention-4's conditional rescale): below that
+    // p stays at most 2^8, which bf16 and the fp32 sums carry exactly as
+    // well, and most steps skip the rescale (4-5 % of the kernel's time)
+    if (__ballot(mnew > m + 8.0f) != 0) {
+      // rescale O and l by exp2(m_old - m_new)
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
       lsum *= alpha;
       int base4 = hh << 4;  // byte address of lane 4h
