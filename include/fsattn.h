@@ -201,8 +201,10 @@ typedef struct {
  *   stage 2: P = MX(bf16(b)) per 32 consecutive keys (fit-max E8M0)
  *   O_i += P V, l_i += P 1 (same P); finally O_i / l_i rounded to bf16.
  * FP6/FP4 score products are exact on the matrix core.  E4M3 Q/K are
- * decoded to BF16 (exact) and summed on the BF16 matrix core from zero, C_i
- * added once in binary32; fsattn_forward_fp8_products keeps the FP8 product.
+ * decoded to BF16 (exact for block scales 2^-124 .. 2^119, that is, for
+ * every block of finite bf16 inputs whose maximum lies between about 2^-116
+ * and 2^127) and summed on the BF16 matrix core from zero, C_i added once in
+ * binary32; fsattn_forward_fp8_products keeps the FP8 product.
  * Errors: FSATTN_E_INVALID_ARG (null, sizes, D not 64/128, kv_tile not a
  * positive multiple of 32, tau < 0, bad enum, prescale/softmax_scale
  * mismatch, bad dump window), FSATTN_E_UNSUPPORTED (format combination,

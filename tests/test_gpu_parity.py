@@ -106,6 +106,21 @@ def test_fp8_products_path(oracle, name, base, kw):
     check_p_fp8_products(res)
 
 
+@pytest.mark.parametrize("qk,ve", [("e2m3", "e2m3"), ("e2m1", "e2m1")])
+def test_fp8_products_entry_is_the_forward_for_other_formats(qk, ve):
+    """FP6/FP4 scores are exact on the matrix core: there the FP8-product entry
+    point runs the default forward, bit for bit."""
+    import softmax_matrix_cores_amd as fs
+    w = W.custom("qknorm-mxfp6", name=f"fp8p-same-{qk}", B=1, H=2, Sq=100, Skv=333, D=128, seed=71,
+                 qk_elem=qk, v_elem=ve, p_elem="e2m3")
+    q, k, v = W.make_inputs(w, device="cuda:0")
+    Q, K, V = fs.quantize_qkv(q, k, v, w.qk_elem, w.v_elem, w.sigma)
+    outs = [fs.forward(Q, K, V, w.B, w.H, w.Sq, w.Skv, w.D, w.sigma, w.p_elem, tau=w.tau, fp8_products=f)
+            for f in (False, True)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
 # the Schraudolph shift c != 0 (60801/8192, the RMS-optimal shift in BF16
 # pattern units) moves T0, the gate threshold and every stage-1 pattern
 @pytest.mark.parametrize("elems", [("e2m3", "e2m3", "e2m3"), ("e2m1", "e2m1", "e2m3"), ("e4m3", "e4m3", "e4m3")])
