@@ -129,6 +129,28 @@ def test_masked_forward_validation_rejects_before_launch():
     assert call(None, _params(B=0)) == 0                              # NULL mask = fsattn_forward
 
 
+def test_fp8_products_forward_validation_rejects_before_launch():
+    """The FP8-product entry point shares the forward's checks (and its NULL mask)."""
+    k1 = _mx(prescale=1.0)
+    v1 = _mx(prescale=1.0)
+    F = fs.lib().fsattn_forward_fp8_products
+
+    def call(mask, p=None, q=None):
+        p = _params() if p is None else p
+        q = _mx() if q is None else q
+        return F(ctypes.byref(p), ctypes.byref(mask) if mask is not None else None, ctypes.byref(q),
+                 ctypes.byref(k1), ctypes.byref(v1), 16, None)
+
+    assert F(None, None, None, None, None, None, None) == -1
+    assert call(None, _params(D=96)) == -1                            # head dim
+    assert call(None, _params(kv_tile=96)) == -2                      # gate tile the kernels do not run
+    assert call(fs._Mask(2, None, None)) == -1                        # causal must be 0 or 1
+    assert call(None, _params(p_elem=4)) == -2                        # FP4 P: only the EFQ-style entry point
+    assert call(None, q=_mx(prescale=3.0)) == -1                      # fold prescale mismatch
+    assert call(None, _params(Sq=0)) == 0                             # empty: OK, no launch
+    assert call(fs._Mask(1, 16, 16), _params(B=0)) == 0
+
+
 def test_rmsnorm_quantize_validation():
     R = fs.lib().fsattn_quantize_mx_rmsnorm
     f = ctypes.c_float
