@@ -90,7 +90,7 @@ def p_mismatch(gc, gs, oc, os_) -> float:
 
 def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=None, kv_tile=None,
              check_quant=True, causal=False, q_lens=None, kv_lens=None, efq=None, gate="exact", c=0.0,
-             more_dumps=(), fp8_products=False):
+             more_dumps=(), fp8_products=False, transform=None):
     """Full comparison on workload w.  rows: oracle row sample (None = all rows).
     causal / q_lens / kv_lens: masks ([B] lists), sent to both sides.
     efq = (tau, h) for E2M1 P (default: the library's calibrated pair).
@@ -100,6 +100,8 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
     fp8_products: E4M3 Q/K scores from the FP8 matrix core
     (fsattn_forward_fp8_products); the P-code comparison then also records
     how many differing codes explain_fp8 explains.
+    transform: optional (q, k, v) -> (q, k, v) applied to the bf16 inputs of
+    both sides.
     Returns a dict of metrics; asserts nothing."""
     masked = causal or q_lens is not None or kv_lens is not None
     if w.p_elem == "e2m1" and efq is None:
@@ -110,6 +112,8 @@ def run_case(O, w: W.Workload, rows=None, dump_head=(0, 0), dump_rows=None, tau=
         + (f" efq={efq}" if efq is not None else "") + (f" gate={gate}" if gate != "exact" else "")
         + (f" c={c}" if c else ""))
     q, k, v = (x.cpu() for x in W.make_inputs(w, device="cuda:0"))
+    if transform is not None:
+        q, k, v = transform(q, k, v)
     tau_ = w.tau if tau is None else tau
     kvt = w.kv_tile if kv_tile is None else kv_tile
     res = {"qk_elem": w.qk_elem}

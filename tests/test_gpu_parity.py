@@ -121,6 +121,31 @@ def test_fp8_products_entry_is_the_forward_for_other_formats(qk, ve):
     assert torch.equal(outs[0], outs[1])
 
 
+def _block_scaled(q, k, v):
+    """Feature block b of Q times 2^(8b), of K times 2^(-8b): every product
+    q_d k_d is unchanged, but the four block scales of a row differ by 2^8
+    steps, so a block scale applied to the wrong block changes the scores."""
+    D = q.shape[-1]
+    f = 2.0 ** (8 * (torch.arange(D) // 32).float())
+    return (q.float() * f).to(torch.bfloat16), (k.float() / f).to(torch.bfloat16), v
+
+
+@pytest.mark.parametrize("qk,ve,pe,fp8p", [("e4m3", "e4m3", "e4m3", False), ("e4m3", "e4m3", "e4m3", True),
+                                         ("e2m3", "e2m3", "e2m3", False), ("e2m1", "e2m1", "e2m3", False)],
+                         ids=["e4m3", "e4m3-fp8-products", "e2m3", "e2m1"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_scales_differ_across_features(oracle, qk, ve, pe, fp8p, D):
+    w = W.custom("stress-mxfp8", name=f"bscale-{qk}", B=1, H=2, Sq=96, Skv=300, D=D, seed=81, qk_elem=qk,
+                 v_elem=ve, p_elem=pe)
+    res = run_case(oracle, w, dump_head=(0, 1), dump_rows=(0, 48), fp8_products=fp8p, transform=_block_scaled)
+    assert_ok(res, defer_p=True)
+    assert res["total_counts"] > 0, res
+    if fp8p:
+        check_p_fp8_products(res)
+    else:
+        check_p(res)
+
+
 # the Schraudolph shift c != 0 (60801/8192, the RMS-optimal shift in BF16
 # pattern units) moves T0, the gate threshold and every stage-1 pattern
 @pytest.mark.parametrize("elems", [("e2m3", "e2m3", "e2m3"), ("e2m1", "e2m1", "e2m3"), ("e4m3", "e4m3", "e4m3")])
