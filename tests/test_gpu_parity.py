@@ -124,10 +124,14 @@ def test_fp8_products_entry_is_the_forward_for_other_formats(qk, ve):
 def _block_scaled(q, k, v):
     """Feature block b of Q times 2^(8b), of K times 2^(-8b): every product
     q_d k_d is unchanged, but the four block scales of a row differ by 2^8
-    steps, so a block scale applied to the wrong block changes the scores."""
-    D = q.shape[-1]
+    steps, so a block scale applied to the wrong block changes the scores.
+    V's key block j (blocks run along keys) times 2^(4 (j mod 4)): its block
+    scales differ from one key block to the next as well."""
+    D, Skv = q.shape[-1], k.shape[-2]
     f = 2.0 ** (8 * (torch.arange(D) // 32).float())
-    return (q.float() * f).to(torch.bfloat16), (k.float() / f).to(torch.bfloat16), v
+    g = 2.0 ** (4 * ((torch.arange(Skv) // 32) % 4).float()).view(-1, 1)
+    return ((q.float() * f).to(torch.bfloat16), (k.float() / f).to(torch.bfloat16),
+            (v.float() * g).to(torch.bfloat16))
 
 
 @pytest.mark.parametrize("qk,ve,pe,fp8p", [("e4m3", "e4m3", "e4m3", False), ("e4m3", "e4m3", "e4m3", True),
