@@ -134,6 +134,22 @@ def _block_scaled(q, k, v):
             (v.float() * g).to(torch.bfloat16))
 
 
+def _far_scales(q, k, v):
+    """Q times 2^-100 and K times 2^100: products unchanged, block scales near
+    2^-104 and 2^96 (inside the range the E4M3 decode is exact for)."""
+    return ((q.float() * 2.0 ** -100).to(torch.bfloat16), (k.float() * 2.0 ** 100).to(torch.bfloat16), v)
+
+
+@pytest.mark.parametrize("qk,ve,pe", [("e4m3", "e4m3", "e4m3"), ("e2m3", "e2m3", "e2m3")])
+def test_far_block_scales(oracle, qk, ve, pe):
+    w = W.custom("stress-mxfp8", name=f"farscale-{qk}", B=1, H=2, Sq=96, Skv=300, D=128, seed=82, qk_elem=qk,
+                 v_elem=ve, p_elem=pe)
+    res = run_case(oracle, w, dump_head=(0, 1), dump_rows=(0, 48), transform=_far_scales)
+    assert_ok(res, defer_p=True)
+    assert res["total_counts"] > 0, res
+    check_p(res)
+
+
 @pytest.mark.parametrize("qk,ve,pe,fp8p", [("e4m3", "e4m3", "e4m3", False), ("e4m3", "e4m3", "e4m3", True),
                                          ("e2m3", "e2m3", "e2m3", False), ("e2m1", "e2m1", "e2m3", False)],
                          ids=["e4m3", "e4m3-fp8-products", "e2m3", "e2m1"])

@@ -71,3 +71,25 @@ def test_quantizer_axis1_shapes(oracle, elem, shape):
     o = oracle.quantize_mx(bits(x[..., :cols]), 1, oracle.ELEM_NAMES[elem], prescale=pre)
     g = fs.MXTensor(codes, scales, e, pre)
     assert same_bytes(g, o, axis=1) == (True, True)
+
+
+@pytest.mark.parametrize("elem", ["e2m3", "e4m3"])
+def test_quantizer_axis1_unaligned_scales(oracle, elem):
+    """A scale buffer that is not 16-byte aligned takes the column-per-lane
+    axis-1 kernel instead of the staged one: the same bytes as the oracle."""
+    import ctypes
+
+    n, rows, cols = 2, 100, 128
+    x = _inputs(n, rows, cols, 350 + ELEMS.index(elem))
+    e = fs.ELEMS[elem]
+    cb, sb = fs.mx_sizes(e, n, rows, cols, 1)
+    codes = torch.zeros(cb, dtype=torch.uint8, device="cuda")
+    sbuf = torch.zeros(sb + 16, dtype=torch.uint8, device="cuda")
+    st = fs.lib().fsattn_quantize_mx(x.cuda().data_ptr(), n, rows, cols, cols, 1, ctypes.c_float(1.0), e,
+                                     fs.SCALE_FITMAX, codes.data_ptr(), sbuf.data_ptr() + 1,
+                                     torch.cuda.current_stream().cuda_stream)
+    assert st == 0, fs.lib().fsattn_status_str(st)
+    torch.cuda.synchronize()
+    o = oracle.quantize_mx(bits(x), 1, oracle.ELEM_NAMES[elem], prescale=1.0)
+    g = fs.MXTensor(codes, sbuf[1:sb + 1].clone(), e, 1.0)
+    assert same_bytes(g, o, axis=1) == (True, True)
